@@ -1,0 +1,383 @@
+// C ABI of libmxfp4.so (declared in include/mxfp4.h): argument checks on the
+// host, kernel choice by shape, launches on the caller's stream.  No
+// allocation, no synchronisation, no CPU fallback.
+//
+// The checks mirror the refusals of the pages' entry points: matmat in
+// "cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs" (b == 0, rows == 0,
+// cols % 32 != 0, short or mis-shaped buffers) and run_stages in
+// "cortiq-engine 0.8.77, src/qtensor/moe_fast.rs" (empty groups, length
+// mismatches, out-of-range indices).  Every check runs before any HIP call,
+// so refusals work on a machine without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/mxfp4.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_tensor(const char *name, const void *w, int64_t rows, int64_t cols)
+{
+    if (!w)
+        return fail(MXFP4_EINVAL, "%s: null pointer", name);
+    if (!aligned(w, 16))
+        return fail(MXFP4_EALIGN, "%s: pointer not 16-byte aligned", name);
+    if (rows < 1 || rows > MXFP4_MAX_ROWS)
+        return fail(MXFP4_EINVAL, "%s: rows = %lld outside [1, %d]", name, (long long)rows,
+                    MXFP4_MAX_ROWS);
+    if (cols < 32 || cols > MXFP4_MAX_COLS || cols % 32 != 0)
+        return fail(MXFP4_EINVAL, "%s: cols = %lld must be a multiple of 32 in [32, %d]", name,
+                    (long long)cols, MXFP4_MAX_COLS);
+    if (mxfp4_nbytes(rows, cols) > MXFP4_MAX_TENSOR_BYTES)
+        return fail(MXFP4_EINVAL, "%s: %lld x %lld exceeds %lld bytes", name, (long long)rows,
+                    (long long)cols, (long long)MXFP4_MAX_TENSOR_BYTES);
+    return MXFP4_OK;
+}
+
+int check_dtype(const char *name, int dt)
+{
+    if (dt != MXFP4_F32 && dt != MXFP4_BF16)
+        return fail(MXFP4_EINVAL, "%s: dtype %d is neither MXFP4_F32 nor MXFP4_BF16", name, dt);
+    return MXFP4_OK;
+}
+
+int check_buffer(const char *name, const void *p, uintptr_t align)
+{
+    if (!p)
+        return fail(MXFP4_EINVAL, "%s: null pointer", name);
+    if (!aligned(p, align))
+        return fail(MXFP4_EALIGN, "%s: pointer not %d-byte aligned", name, (int)align);
+    return MXFP4_OK;
+}
+
+int launched(hipError_t st, const char *what)
+{
+    if (st != hipSuccess)
+        return fail(MXFP4_ELAUNCH, "%s: %s", what, hipGetErrorString(st));
+    return MXFP4_OK;
+}
+
+#define TRY(x)                                                                                     \
+    do {                                                                                           \
+        int _s = (x);                                                                              \
+        if (_s != MXFP4_OK)                                                                        \
+            return _s;                                                                             \
+    } while (0)
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Workspace layout of the expert bank.
+struct MoeLayout {
+    size_t offsets, pair_of_slot, slot_of_pair, token_of_slot, work, n_work, h, y, total;
+};
+
+MoeLayout moe_layout(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t hidden,
+                     int64_t inter, int x_dtype)
+{
+    const int64_t P = n_tokens * top_k;
+    MoeLayout L;
+    size_t o = 0;
+    L.offsets = o;
+    o += align256((size_t)(n_experts + 1) * 4);
+    L.pair_of_slot = o;
+    o += align256((size_t)P * 4);
+    L.slot_of_pair = o;
+    o += align256((size_t)P * 4);
+    L.token_of_slot = o;
+    o += align256((size_t)P * 4);
+    L.work = o;
+    o += align256((size_t)P * 16); // at most one item per pair
+    L.n_work = o;
+    o += 256;
+    L.h = o;
+    o += align256((size_t)P * inter * (x_dtype == MXFP4_BF16 ? 2 : 4));
+    L.y = o;
+    o += align256((size_t)P * hidden * 4);
+    L.total = o;
+    return L;
+}
+
+int check_moe(const void *gate, const void *up, const void *down, int64_t n_experts,
+              int64_t hidden, int64_t inter, const void *x, int x_dtype, int64_t n_tokens,
+              const int32_t *topk_ids, const float *topk_w, int64_t top_k, void *out,
+              int out_dtype, bool need_out, void *workspace, size_t workspace_bytes)
+{
+    if (n_experts < 1 || n_experts > MXFP4_MAX_EXPERTS)
+        return fail(MXFP4_EINVAL, "n_experts = %lld outside [1, %d]", (long long)n_experts,
+                    MXFP4_MAX_EXPERTS);
+    if (top_k < 1 || top_k > MXFP4_MAX_TOP_K || top_k > n_experts)
+        return fail(MXFP4_EINVAL, "top_k = %lld outside [1, min(%d, n_experts)]",
+                    (long long)top_k, MXFP4_MAX_TOP_K);
+    if (n_tokens < 1 || n_tokens > MXFP4_MAX_TOKENS)
+        return fail(MXFP4_EINVAL, "n_tokens = %lld outside [1, %d]", (long long)n_tokens,
+                    MXFP4_MAX_TOKENS);
+    TRY(check_tensor("gate", gate, inter, hidden));
+    TRY(check_tensor("up", up, inter, hidden));
+    TRY(check_tensor("down", down, hidden, inter));
+    if (mxfp4_nbytes(inter, hidden) % 16 != 0)
+        return fail(MXFP4_EALIGN, "expert tensor size %lld is not a multiple of 16 bytes",
+                    (long long)mxfp4_nbytes(inter, hidden));
+    TRY(check_dtype("x_dtype", x_dtype));
+    TRY(check_buffer("x", x, 16));
+    TRY(check_buffer("topk_ids", topk_ids, 4));
+    TRY(check_buffer("topk_w", topk_w, 4));
+    if (need_out) {
+        TRY(check_dtype("out_dtype", out_dtype));
+        TRY(check_buffer("out", out, 16));
+    }
+    TRY(check_buffer("workspace", workspace, 16));
+    const size_t need = moe_layout(n_tokens, top_k, n_experts, hidden, inter, x_dtype).total;
+    if (workspace_bytes < need)
+        return fail(MXFP4_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    const int64_t P = n_tokens * top_k;
+    const int64_t nrb = (hidden + 63) / 64;
+    if (P * nrb > ((int64_t)1 << 31) - 1)
+        return fail(MXFP4_EINVAL, "n_tokens * top_k * hidden/64 too large for one launch");
+    return MXFP4_OK;
+}
+
+int moe_run(const void *gate, const void *up, const void *down, int64_t n_experts, int64_t hidden,
+            int64_t inter, const void *x, int x_dtype, int64_t n_tokens, const int32_t *topk_ids,
+            const float *topk_w, int64_t top_k, void *out, int out_dtype, void *workspace,
+            const void *h_in, void *h_out, hipStream_t st)
+{
+    const bool xbf = x_dtype == MXFP4_BF16;
+    const int P = (int)(n_tokens * top_k);
+    const MoeLayout L = moe_layout(n_tokens, top_k, n_experts, hidden, inter, x_dtype);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+    int32_t *pos = reinterpret_cast<int32_t *>(ws + L.pair_of_slot);
+    int32_t *slot = reinterpret_cast<int32_t *>(ws + L.slot_of_pair);
+    int32_t *tos = reinterpret_cast<int32_t *>(ws + L.token_of_slot);
+    int32_t *work = reinterpret_cast<int32_t *>(ws + L.work);
+    int32_t *n_work = reinterpret_cast<int32_t *>(ws + L.n_work);
+    void *h = ws + L.h;
+    float *y = reinterpret_cast<float *>(ws + L.y);
+
+    // tokens per work item: every token of an expert in one item when it fits
+    int want = (int)(n_tokens < 16 ? n_tokens : 16);
+    int tpc_gu = mx::skinny_pick_tpc(mx::MODE_GATEUP, xbf, (int)hidden, want);
+    int tpc_dn = mx::skinny_pick_tpc(mx::MODE_DOWN, xbf, (int)inter, want);
+    const int tpc = tpc_gu < tpc_dn ? tpc_gu : tpc_dn;
+    if (tpc < 1)
+        return fail(MXFP4_EINVAL, "hidden/inter too large for the on-chip operand buffers");
+    const int max_work = mx::group_max_work(P, (int)n_experts, tpc);
+
+    mx::GroupArgs g;
+    g.ids = topk_ids;
+    g.n_pairs = P;
+    g.top_k = (int)top_k;
+    g.n_experts = (int)n_experts;
+    g.tpc = tpc;
+    g.offsets = offsets;
+    g.pair_of_slot = pos;
+    g.slot_of_pair = slot;
+    g.token_of_slot = tos;
+    g.work = work;
+    g.n_work = n_work;
+    TRY(launched(mx::group_launch(g, st), "group"));
+
+    const int64_t tbytes = mxfp4_nbytes(inter, hidden);
+    if (!h_in) {
+        mx::SkinnyArgs a = {};
+        a.w0 = static_cast<const uint8_t *>(gate);
+        a.w1 = static_cast<const uint8_t *>(up);
+        a.expert_stride = tbytes;
+        a.rows = (int)inter;
+        a.cols = (int)hidden;
+        a.x = x;
+        a.nch = max_work;
+        a.y = h;
+        a.y_bf16 = xbf;
+        a.work = work;
+        a.n_work = n_work;
+        a.token_of_slot = tos;
+        const int nrb = (int)((inter + mx::skinny_rows_per_wg(mx::MODE_GATEUP) - 1) /
+                              mx::skinny_rows_per_wg(mx::MODE_GATEUP));
+        TRY(launched(mx::skinny_launch(mx::MODE_GATEUP, xbf, tpc, a, dim3(nrb * max_work), st),
+                     "gate/up"));
+        if (h_out)
+            TRY(launched(mx::copy_launch(h_out, h, (size_t)P * inter * (xbf ? 2 : 4), st),
+                         "h copy"));
+    }
+    if (!out)
+        return MXFP4_OK;
+    {
+        mx::SkinnyArgs a = {};
+        a.w0 = static_cast<const uint8_t *>(down);
+        a.expert_stride = tbytes;
+        a.rows = (int)hidden;
+        a.cols = (int)inter;
+        a.x = h_in ? h_in : h;
+        a.nch = max_work;
+        a.y = y;
+        a.y_bf16 = 0;
+        a.work = work;
+        a.n_work = n_work;
+        const int nrb = (int)((hidden + mx::skinny_rows_per_wg(mx::MODE_DOWN) - 1) /
+                              mx::skinny_rows_per_wg(mx::MODE_DOWN));
+        TRY(launched(mx::skinny_launch(mx::MODE_DOWN, xbf, tpc, a, dim3(nrb * max_work), st),
+                     "down"));
+    }
+    TRY(launched(mx::combine_launch(y, slot, topk_w, (int)n_tokens, (int)top_k, (int)hidden, out,
+                                    out_dtype == MXFP4_BF16, st),
+                 "combine"));
+    return MXFP4_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int64_t mxfp4_nbytes(int64_t rows, int64_t cols)
+{
+    if (rows < 0 || cols < 0 || cols % 32 != 0)
+        return -1;
+    return rows * (cols / 2) + rows * (cols / 32);
+}
+
+const char *mxfp4_last_error(void) { return g_err; }
+
+int mxfp4_dequant(const void *w, int64_t rows, int64_t cols, void *out, int out_dtype, void *stream)
+{
+    clear_error();
+    TRY(check_tensor("w", w, rows, cols));
+    TRY(check_dtype("out_dtype", out_dtype));
+    TRY(check_buffer("out", out, 16));
+    return launched(mx::dequant_launch(static_cast<const uint8_t *>(w), rows, cols, out,
+                                       out_dtype == MXFP4_BF16, (hipStream_t)stream),
+                    "dequant");
+}
+
+int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_dtype, int64_t b,
+               void *y, int y_dtype, void *stream)
+{
+    clear_error();
+    TRY(check_tensor("w", w, rows, cols));
+    TRY(check_dtype("x_dtype", x_dtype));
+    TRY(check_dtype("y_dtype", y_dtype));
+    if (b < 1 || b > MXFP4_MAX_TOKENS)
+        return fail(MXFP4_EINVAL, "b = %lld outside [1, %d]", (long long)b, MXFP4_MAX_TOKENS);
+    TRY(check_buffer("x", x, 16));
+    TRY(check_buffer("y", y, 16));
+    const bool xbf = x_dtype == MXFP4_BF16;
+    const int maxc = xbf ? 16 : 8;
+    const int tpc = mx::skinny_pick_tpc(mx::MODE_GEMM, xbf, (int)cols, b < maxc ? (int)b : maxc);
+    if (tpc < 1)
+        return fail(MXFP4_EINVAL, "cols = %lld too large for the on-chip operand buffers",
+                    (long long)cols);
+    const int64_t nch = (b + tpc - 1) / tpc;
+    const int rw = mx::skinny_rows_per_wg(mx::MODE_GEMM);
+    const int64_t nrb = (rows + rw - 1) / rw;
+    if (nch * nrb > ((int64_t)1 << 31) - 1)
+        return fail(MXFP4_EINVAL, "rows * b too large for one launch");
+    mx::SkinnyArgs a = {};
+    a.w0 = static_cast<const uint8_t *>(w);
+    a.rows = (int)rows;
+    a.cols = (int)cols;
+    a.x = x;
+    a.b = (int)b;
+    a.nch = (int)nch;
+    a.y = y;
+    a.y_bf16 = y_dtype == MXFP4_BF16;
+    return launched(mx::skinny_launch(mx::MODE_GEMM, xbf, tpc, a, dim3((unsigned)(nch * nrb)),
+                                      (hipStream_t)stream),
+                    "gemm");
+}
+
+int mxfp4_matvec(const void *w, int64_t rows, int64_t cols, const float *x, float *y, void *stream)
+{
+    return mxfp4_gemm(w, rows, cols, x, MXFP4_F32, 1, y, MXFP4_F32, stream);
+}
+
+int moe_route_group(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k, int64_t n_experts,
+                    int32_t *offsets, int32_t *pair_of_slot, int32_t *slot_of_pair, void *stream)
+{
+    clear_error();
+    if (n_experts < 1 || n_experts > MXFP4_MAX_EXPERTS)
+        return fail(MXFP4_EINVAL, "n_experts = %lld outside [1, %d]", (long long)n_experts,
+                    MXFP4_MAX_EXPERTS);
+    if (top_k < 1 || top_k > MXFP4_MAX_TOP_K)
+        return fail(MXFP4_EINVAL, "top_k = %lld outside [1, %d]", (long long)top_k,
+                    MXFP4_MAX_TOP_K);
+    if (n_tokens < 1 || n_tokens > MXFP4_MAX_TOKENS)
+        return fail(MXFP4_EINVAL, "n_tokens = %lld outside [1, %d]", (long long)n_tokens,
+                    MXFP4_MAX_TOKENS);
+    TRY(check_buffer("topk_ids", topk_ids, 4));
+    TRY(check_buffer("offsets", offsets, 4));
+    TRY(check_buffer("pair_of_slot", pair_of_slot, 4));
+    TRY(check_buffer("slot_of_pair", slot_of_pair, 4));
+    mx::GroupArgs g = {};
+    g.ids = topk_ids;
+    g.n_pairs = (int)(n_tokens * top_k);
+    g.top_k = (int)top_k;
+    g.n_experts = (int)n_experts;
+    g.tpc = 1;
+    g.offsets = offsets;
+    g.pair_of_slot = pair_of_slot;
+    g.slot_of_pair = slot_of_pair;
+    return launched(mx::group_launch(g, (hipStream_t)stream), "group");
+}
+
+size_t moe_experts_mxfp4_workspace_size(int64_t n_tokens, int64_t top_k, int64_t n_experts,
+                                        int64_t hidden, int64_t inter, int x_dtype)
+{
+    if (n_tokens < 1 || top_k < 1 || n_experts < 1 || hidden < 32 || inter < 32 ||
+        hidden % 32 || inter % 32 || (x_dtype != MXFP4_F32 && x_dtype != MXFP4_BF16) ||
+        n_tokens > MXFP4_MAX_TOKENS || top_k > MXFP4_MAX_TOP_K || n_experts > MXFP4_MAX_EXPERTS ||
+        hidden > MXFP4_MAX_COLS || inter > MXFP4_MAX_COLS)
+        return 0;
+    return moe_layout(n_tokens, top_k, n_experts, hidden, inter, x_dtype).total;
+}
+
+int moe_experts_mxfp4(const void *gate, const void *up, const void *down, int64_t n_experts,
+                      int64_t hidden, int64_t inter, const void *x, int x_dtype, int64_t n_tokens,
+                      const int32_t *topk_ids, const float *topk_w, int64_t top_k, void *out,
+                      int out_dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    clear_error();
+    TRY(check_moe(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
+                  topk_w, top_k, out, out_dtype, true, workspace, workspace_bytes));
+    return moe_run(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
+                   topk_w, top_k, out, out_dtype, workspace, nullptr, nullptr,
+                   (hipStream_t)stream);
+}
+
+int moe_experts_mxfp4_stages(const void *gate, const void *up, const void *down,
+                             int64_t n_experts, int64_t hidden, int64_t inter, const void *x,
+                             int x_dtype, int64_t n_tokens, const int32_t *topk_ids,
+                             const float *topk_w, int64_t top_k, void *out, int out_dtype,
+                             void *workspace, size_t workspace_bytes, const void *h_in,
+                             void *h_out, void *stream)
+{
+    clear_error();
+    TRY(check_moe(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
+                  topk_w, top_k, out, out_dtype, out != nullptr, workspace, workspace_bytes));
+    if (!out && !h_out)
+        return fail(MXFP4_EINVAL, "stages: nothing requested (out and h_out are both null)");
+    if (h_in)
+        TRY(check_buffer("h_in", h_in, 16));
+    if (h_out)
+        TRY(check_buffer("h_out", h_out, 16));
+    if (h_in && h_out)
+        return fail(MXFP4_EINVAL, "stages: h_in and h_out are exclusive");
+    return moe_run(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
+                   topk_w, top_k, out, out_dtype, workspace, h_in, h_out, (hipStream_t)stream);
+}
+
+} // extern "C"

@@ -1,0 +1,104 @@
+// Device helpers shared by the gfx950 kernels of libmxfp4.
+//
+// Format decode uses the CDNA4 conversion instructions
+// v_cvt_scalef32_pk_{f32,bf16}_fp4: they read two E2M1 nibbles of a byte
+// (low nibble first) and scale them by 2^(E-127), E being the exponent field
+// of the fp32 scale operand.  Passing the E8M0 byte k as (k << 23) therefore
+// applies the format's scale exactly, including k = 0 (2^-127) and k = 255
+// (NaN); the products are rounded once (exact for every finite weight).
+// This is the decode of the DECODE shader (mx_e2m1, mx_e8m0) of
+// "cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs", done by the hardware.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 scale operand carrying E8M0 byte k in its exponent field.
+__device__ __forceinline__ float e8m0_operand(uint32_t k) { return __uint_as_float(k << 23); }
+
+// Byte `idx` (0..3) of a word, as the scale operand.
+__device__ __forceinline__ float e8m0_operand_of(uint32_t word, uint32_t idx)
+{
+    return __uint_as_float(((word >> (8u * idx)) & 0xFFu) << 23);
+}
+
+// Eight weights (one code word, nibbles 0..7 = elements 0..7) as bf16,
+// scaled: the MFMA A/B operand of one lane.
+__device__ __forceinline__ bf16x8 decode8_bf16(uint32_t word, float scale)
+{
+    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
+    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
+    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2);
+    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// Eight weights as fp32 (two per conversion).
+__device__ __forceinline__ void decode8_f32(uint32_t word, float scale, float *out)
+{
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, 3);
+    out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
+    out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
+}
+
+// 16x16x32 bf16 MFMA with fp32 accumulate.  Lane l holds A row l%16,
+// k = 8*(l/16)..+8; B column l%16, same k; D column l%16, rows
+// 4*(l/16)..+4.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Exact split of fp32 into bf16 hi + lo for 8 values: hi = RNE(x),
+// lo = RNE(x - hi) (x - hi is exact in fp32); |x - hi - lo| <= 2^-16 |x|.
+__device__ __forceinline__ void split_bf16x8(const float *x, bf16x8 &hi, bf16x8 &lo)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f32x2 v = {x[2 * i], x[2 * i + 1]};
+        bf16x2 h = __builtin_convertvector(v, bf16x2);
+        uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        f32x2 hf = {__uint_as_float(hb << 16), __uint_as_float(hb & 0xFFFF0000u)};
+        f32x2 r = {v[0] - hf[0], v[1] - hf[1]};
+        bf16x2 l = __builtin_convertvector(r, bf16x2);
+        hi[2 * i] = h[0];
+        hi[2 * i + 1] = h[1];
+        lo[2 * i] = l[0];
+        lo[2 * i + 1] = l[1];
+    }
+}
+
+// Round fp32 to bf16, nearest-even (v_cvt_pk_bf16_f32); inf/NaN kept.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v)
+{
+    f32x2 p = {v, 0.0f};
+    bf16x2 h = __builtin_convertvector(p, bf16x2);
+    return (uint16_t)(__builtin_bit_cast(uint32_t, h) & 0xFFFFu);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// DPP rotate by 8 within each 16-lane row: lane l reads lane (l & ~15) | ((l + 8) & 15).
+__device__ __forceinline__ float dpp_row_ror8(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+} // namespace mx

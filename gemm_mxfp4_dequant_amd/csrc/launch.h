@@ -1,0 +1,61 @@
+// Internal interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mx {
+
+enum { MODE_GEMM = 0, MODE_GATEUP = 1, MODE_DOWN = 2 };
+
+// Arguments of the skinny MFMA kernels (one struct for all modes).
+struct SkinnyArgs {
+    const uint8_t *w0;        // GEMM: the tensor; GATEUP: gate bank; DOWN: down bank
+    const uint8_t *w1;        // GATEUP: up bank
+    int64_t expert_stride;    // bytes between experts in a bank
+    int rows, cols;           // of one tensor
+    const void *x;            // GEMM: x [b][cols]; GATEUP: x [T][cols]; DOWN: h [slots][cols]
+    int b;                    // GEMM: tokens
+    int nch;                  // grid = row blocks * nch (GEMM: token chunks; MoE: item bound)
+    void *y;                  // GEMM: y [b][rows]; GATEUP: h [slots][rows]; DOWN: y [slots][rows]
+    int y_bf16;               // output element type (GEMM, GATEUP)
+    const int *work;          // MoE: int4 {expert, first slot, tokens, 0} per item
+    const int *n_work;        // MoE: number of items (device)
+    const int *token_of_slot; // GATEUP: token row of each slot
+};
+
+int skinny_rows_per_wg(int mode);
+// Tokens per workgroup for a call that wants `want` columns (fits LDS).
+int skinny_pick_tpc(int mode, bool xbf, int cols, int want);
+size_t skinny_lds_bytes(int mode, bool xbf, int cols, int tpc);
+hipError_t skinny_launch(int mode, bool xbf, int tpc, const SkinnyArgs &a, dim3 grid,
+                         hipStream_t stream);
+
+hipError_t dequant_launch(const uint8_t *w, int64_t rows, int64_t cols, void *out, bool bf16,
+                          hipStream_t stream);
+
+// Grouping of pairs by expert (one workgroup) and the work list for the
+// expert kernels.  ws_* are device arrays inside the caller's workspace.
+struct GroupArgs {
+    const int32_t *ids;
+    int n_pairs, top_k, n_experts, tpc;
+    int32_t *offsets;       // [E+1]
+    int32_t *pair_of_slot;  // [P]
+    int32_t *slot_of_pair;  // [P]
+    int32_t *token_of_slot; // [P] (may be null)
+    int32_t *work;          // [max_work][4] (may be null)
+    int32_t *n_work;        // [1] (may be null)
+};
+hipError_t group_launch(const GroupArgs &g, hipStream_t stream);
+int group_max_work(int n_pairs, int n_experts, int tpc);
+
+// out[t][r] = sum_k w[t][k] * y[slot_of_pair[t*K+k]][r]
+hipError_t combine_launch(const float *y, const int32_t *slot_of_pair, const float *w,
+                          int n_tokens, int top_k, int hidden, void *out, bool out_bf16,
+                          hipStream_t stream);
+
+// Copy h rows (slot order) between a caller buffer and the workspace.
+hipError_t copy_launch(void *dst, const void *src, size_t bytes, hipStream_t stream);
+
+} // namespace mx

@@ -1,0 +1,150 @@
+/*
+ * mxfp4.h - C ABI of libmxfp4.so: fused MXFP4 dequantize-and-multiply on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Weight format (OCP MX FP4), as stored by the pages this implements
+ * ("cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs": module doc, DECODE and
+ * PEROP shaders, MoeBankCodec::lens):
+ *   A rows x cols tensor (cols % 32 == 0) is rows*cols/2 code bytes followed
+ *   by rows*cols/32 scale bytes, rows*cols*17/32 bytes in all.
+ *   - Code plane, row-major: element (r, c) is nibble c&1 (low nibble first)
+ *     of byte (r*cols + c)/2.  A code n is E2M1: (-1)^(n>>3) times
+ *     {0, 0.5, 1, 1.5, 2, 3, 4, 6}[n & 7] (code 8 is -0).
+ *   - Scale plane, row-major: byte r*(cols/32) + c/32 is the E8M0 scale k of
+ *     the 32-element group holding (r, c): 2^(k-127); k = 255 is NaN and
+ *     k = 0 is 2^-127.
+ *   - The weight is the E2M1 value times its scale.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named w, gate, up, down, x, y, out, workspace are DEVICE
+ *     pointers owned by the caller and must be 16-byte aligned; topk_ids
+ *     and topk_w are device pointers, 4-byte aligned.
+ *   - stream is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *     kernels on it and return: no host synchronisation, no allocation, no
+ *     pointer kept after return.
+ *   - Arguments are checked on the host before anything is launched.  On
+ *     failure nothing is launched and a negative status is returned; the
+ *     message is available from mxfp4_last_error() (per thread).
+ *   - There is no CPU fallback: every result is computed by HIP kernels.
+ *   - Activations/outputs are row-major: x [b][cols], y [b][rows].
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MXFP4_OK 0
+#define MXFP4_EINVAL (-1)     /* bad size, dtype, null pointer or out-of-range argument */
+#define MXFP4_EALIGN (-2)     /* a pointer is not aligned as documented */
+#define MXFP4_EWORKSPACE (-3) /* workspace smaller than the size query returned */
+#define MXFP4_ELAUNCH (-4)    /* the HIP runtime refused a launch */
+
+/* Element types of activations and outputs. */
+#define MXFP4_F32 0
+#define MXFP4_BF16 1
+
+/* Largest accepted sizes (checked; larger calls return MXFP4_EINVAL). */
+#define MXFP4_MAX_ROWS (1 << 24)
+#define MXFP4_MAX_COLS (1 << 14)
+#define MXFP4_MAX_TENSOR_BYTES ((int64_t)1 << 31) /* one rows x cols tensor */
+#define MXFP4_MAX_TOKENS (1 << 20)
+#define MXFP4_MAX_EXPERTS 1024
+#define MXFP4_MAX_TOP_K 32
+
+/* Byte size of a rows x cols tensor, rows*cols*17/32; -1 if cols % 32 != 0
+ * or a size is negative.  Host only. */
+int64_t mxfp4_nbytes(int64_t rows, int64_t cols);
+
+/* Dequantize W (rows x cols) to out [rows][cols] of out_dtype (MXFP4_F32 or
+ * MXFP4_BF16).  Bit-exact: every finite weight is exactly representable in
+ * both types; overflow gives +-inf; a scale-255 group gives 0x7FC00000
+ * (fp32) / 0x7FC0 (bf16) for every element.  Follows the DECODE shader
+ * (mx_e2m1, mx_e8m0) of "cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs".
+ * rows >= 1, cols >= 32. */
+int mxfp4_dequant(const void *w, int64_t rows, int64_t cols, void *out, int out_dtype,
+                  void *stream);
+
+/* Decode matvec: y[r] = sum_c W[r][c] * x[c], fp32 in and out.
+ * "cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs", matmat with b = 1
+ * (mxfp4_mv).  Same kernel and same result, bit for bit, as mxfp4_gemm
+ * with b = 1. */
+int mxfp4_matvec(const void *w, int64_t rows, int64_t cols, const float *x, float *y,
+                 void *stream);
+
+/* Small-batch GEMM: y[t][r] = sum_c W[r][c] * x[t][c] for t < b.
+ * x is [b][cols] of x_dtype, y is [b][rows] of y_dtype (fp32 accumulate).
+ * "cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs", matmat (mxfp4_mm).
+ * Each token's row equals, bit for bit, what the same call gives for that
+ * token alone.  b >= 1. */
+int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_dtype, int64_t b,
+               void *y, int y_dtype, void *stream);
+
+/* Stable grouping of routed pairs by expert (the first step of the expert
+ * bank), exposed for callers and tests.  Pairs are p = t*top_k + k.
+ *   offsets [n_experts+1]: pairs of expert e occupy slots
+ *       offsets[e] .. offsets[e+1]-1, in increasing p;
+ *   pair_of_slot [n_tokens*top_k]: the pair in each slot;
+ *   slot_of_pair [n_tokens*top_k]: the slot of each pair, -1 for a pair
+ *       whose id is outside [0, n_experts) (such a pair is dropped).
+ * "rlx-cpu 0.2.17, src/gguf_matmul.rs", grouped_moe_sort_plan. */
+int moe_route_group(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k, int64_t n_experts,
+                    int32_t *offsets, int32_t *pair_of_slot, int32_t *slot_of_pair,
+                    void *stream);
+
+/* Workspace bytes moe_experts_mxfp4 needs for these sizes (0 on bad sizes). */
+size_t moe_experts_mxfp4_workspace_size(int64_t n_tokens, int64_t top_k, int64_t n_experts,
+                                        int64_t hidden, int64_t inter, int x_dtype);
+
+/* Routed expert bank.  For each token t and slot k (pair p = t*top_k + k)
+ * with expert e = topk_ids[p]:
+ *     g = W_gate[e] x_t,  u = W_up[e] x_t        (W_gate, W_up: inter x hidden)
+ *     h = silu(g) * u,  silu(g) = g / (1 + e^-g)
+ *     y_p = W_down[e] h                          (W_down: hidden x inter)
+ *     out[t] = sum_k topk_w[p] * y_p             (in slot order, fp32)
+ * gate, up, down: n_experts tensors each, contiguous, stride
+ * mxfp4_nbytes(rows, cols) (which must be a multiple of 16).
+ * x [n_tokens][hidden] of x_dtype; out [n_tokens][hidden] of out_dtype.
+ * The activation h is kept in x_dtype (rounded to bf16, nearest-even, when
+ * x is bf16); accumulation is fp32.  Each expert's weights are streamed
+ * once per call for all of its tokens.  Ids outside [0, n_experts) drop the
+ * pair.  The workspace (device, 16-byte aligned, at least
+ * moe_experts_mxfp4_workspace_size bytes) is scratch owned by the call
+ * until the stream reaches it; it needs no initialisation.
+ * "cortiq-engine 0.8.77, src/qtensor/moe_fast.rs" (gate_up_block,
+ * down_block); "cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs"
+ * (dsv4_global_gate_up_mxfp4, dsv4_global_down_mxfp4, generic f32
+ * weighting, mxg_bf16 rounding); "rlx-cpu 0.2.17, src/gguf_matmul.rs"
+ * (grouped_moe_sort_plan, grouped_moe_unpermute_out). */
+int moe_experts_mxfp4(const void *gate, const void *up, const void *down, int64_t n_experts,
+                      int64_t hidden, int64_t inter, const void *x, int x_dtype, int64_t n_tokens,
+                      const int32_t *topk_ids, const float *topk_w, int64_t top_k, void *out,
+                      int out_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Stage-isolation variant of moe_experts_mxfp4 (the gs_in / gs_out hooks of
+ * "cortiq-engine 0.8.77, src/qtensor/moe_fast.rs", run_stages).  h is in
+ * SLOT order ([n_tokens*top_k][inter] of x_dtype, slot as returned by
+ * moe_route_group); pairs with slot -1 have no row.
+ *   h_out != NULL: after gate/up + SwiGLU, copy h there.
+ *   h_in != NULL : skip gate/up and run down + combine on h_in.
+ *   out may be NULL when only h_out is wanted. */
+int moe_experts_mxfp4_stages(const void *gate, const void *up, const void *down,
+                             int64_t n_experts, int64_t hidden, int64_t inter, const void *x,
+                             int x_dtype, int64_t n_tokens, const int32_t *topk_ids,
+                             const float *topk_w, int64_t top_k, void *out, int out_dtype,
+                             void *workspace, size_t workspace_bytes, const void *h_in,
+                             void *h_out, void *stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *mxfp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

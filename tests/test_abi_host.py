@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every function declared in include/mxfp4.h, and
+refuses bad arguments before touching the GPU (every check runs on the host
+ahead of any HIP call), in the manner of the pages' entry points ("cortiq-
+engine 0.8.40, src/gpu_wgpu/mxfp4.rs", matmat: b == 0, rows == 0,
+cols % 32 != 0, wrong dtype/shape are refused).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+LIB = os.path.join(ROOT, "gemm_mxfp4_dequant_amd", "libmxfp4.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmxfp4.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|int64_t|size_t|char)\s*\*?\s*(\w+)\s*\(", src,
+                       flags=re.M)
+    return names
+
+
+@pytest.fixture(scope="module")
+def m():
+    from gemm_mxfp4_dequant_amd import mxfp4
+    mxfp4.lib()
+    return mxfp4
+
+
+def test_exports_every_declared_symbol(m):
+    names = declared_functions()
+    assert len(names) == 9, names
+    L = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_nbytes(m):
+    assert m.mxfp4_nbytes(2304, 5120) == 2304 * 5120 * 17 // 32
+    assert m.mxfp4_nbytes(1, 32) == 17
+    assert m.mxfp4_nbytes(4, 48) == -1
+    assert m.mxfp4_nbytes(-1, 32) == -1
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: calls below are refused first
+
+
+def status(fn, *args):
+    return fn(*args)
+
+
+@pytest.mark.parametrize("rows,cols,b,xdt,ydt,expect", [
+    (0, 64, 1, 0, 0, -1),        # rows == 0
+    (16, 48, 1, 0, 0, -1),       # cols % 32
+    (16, 0, 1, 0, 0, -1),
+    (16, 64, 0, 0, 0, -1),       # b == 0
+    (16, 64, 1, 2, 0, -1),       # bad x dtype
+    (16, 64, 1, 0, 7, -1),       # bad y dtype
+    (16, 1 << 15, 1, 0, 0, -1),  # cols above the cap
+])
+def test_gemm_refusals(m, rows, cols, b, xdt, ydt, expect):
+    L = m.lib()
+    assert L.mxfp4_gemm(FAKE, rows, cols, FAKE, xdt, b, FAKE, ydt, None) == expect
+    assert m.mxfp4_last_error() != ""
+
+
+def test_alignment_and_null(m):
+    L = m.lib()
+    assert L.mxfp4_gemm(FAKE + 4, 16, 64, FAKE, 0, 1, FAKE, 0, None) == m.MXFP4_EALIGN
+    assert L.mxfp4_gemm(None, 16, 64, FAKE, 0, 1, FAKE, 0, None) == m.MXFP4_EINVAL
+    assert L.mxfp4_gemm(FAKE, 16, 64, FAKE + 8, 0, 1, FAKE, 0, None) == m.MXFP4_EALIGN
+    assert L.mxfp4_matvec(FAKE, 16, 64, None, FAKE, None) == m.MXFP4_EINVAL
+    assert L.mxfp4_dequant(FAKE, 16, 64, FAKE, 3, None) == m.MXFP4_EINVAL
+    assert L.mxfp4_dequant(FAKE, 16, 40, FAKE, 0, None) == m.MXFP4_EINVAL
+    assert "cols" in m.mxfp4_last_error()
+
+
+def test_moe_refusals(m):
+    L = m.lib()
+    ws = m.moe_experts_mxfp4_workspace_size(8, 6, 64, 4096, 2048, 0)
+    assert ws > 8 * 6 * 4096 * 4
+    assert m.moe_experts_mxfp4_workspace_size(8, 6, 64, 4096, 2000, 0) == 0
+    args = dict(E=64, H=4096, I=2048, T=8, K=6)
+
+    def call(E=64, H=4096, I=2048, T=8, K=6, ws_bytes=ws, xdt=0, odt=1, wsp=FAKE, ids=FAKE):
+        return L.moe_experts_mxfp4(FAKE, FAKE, FAKE, E, H, I, FAKE, xdt, T, ids, FAKE, K, FAKE,
+                                   odt, wsp, ws_bytes, None)
+
+    assert call(K=65) == m.MXFP4_EINVAL           # top_k > n_experts
+    assert call(E=0) == m.MXFP4_EINVAL
+    assert call(T=0) == m.MXFP4_EINVAL            # empty
+    assert call(I=2000) == m.MXFP4_EINVAL         # inter % 32
+    assert call(ws_bytes=ws - 1) == m.MXFP4_EWORKSPACE
+    assert call(wsp=FAKE + 4) == m.MXFP4_EALIGN
+    assert call(ids=FAKE + 2) == m.MXFP4_EALIGN
+    assert call(xdt=5) == m.MXFP4_EINVAL
+    assert args
+
+
+def test_stage_refusals(m):
+    L = m.lib()
+    ws = m.moe_experts_mxfp4_workspace_size(4, 2, 8, 512, 256, 0)
+    r = L.moe_experts_mxfp4_stages(FAKE, FAKE, FAKE, 8, 512, 256, FAKE, 0, 4, FAKE, FAKE, 2,
+                                   None, 1, FAKE, ws, None, None, None)
+    assert r == m.MXFP4_EINVAL  # nothing requested
+    r = L.moe_experts_mxfp4_stages(FAKE, FAKE, FAKE, 8, 512, 256, FAKE, 0, 4, FAKE, FAKE, 2,
+                                   FAKE, 1, FAKE, ws, FAKE, FAKE, None)
+    assert r == m.MXFP4_EINVAL  # h_in and h_out together
+
+
+def test_group_refusals(m):
+    L = m.lib()
+    assert L.moe_route_group(FAKE, 4, 2, 0, FAKE, FAKE, FAKE, None) == m.MXFP4_EINVAL
+    assert L.moe_route_group(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, None) == m.MXFP4_EINVAL
+    assert L.moe_route_group(FAKE + 1, 4, 2, 8, FAKE, FAKE, FAKE, None) == m.MXFP4_EALIGN

@@ -1,0 +1,183 @@
+"""GPU parity of the routed expert bank against the oracle.
+
+* grouping (moe_route_group): bit-exact offsets / pair order / slots;
+* stage isolation (moe_experts_mxfp4_stages, after the gs_in / gs_out hooks
+  of "cortiq-engine 0.8.77, src/qtensor/moe_fast.rs", run_stages):
+    h:  |h_gpu - h_or| <= 1e-4 (|silu'(g)| |u| mag_g + |silu(g)| mag_u)
+                          + 4 ulp_f32(h)  [+ 1 ulp_bf16(h) when h is bf16]
+    down + combine fed with h_gpu:
+        |out_gpu - out_or| <= 1e-4 sum_k |w_k| mag_y + 1 ulp_bf16(out_or)
+* end to end: nrmse < 1e-3 and cosine > 0.9999 against the oracle's bf16
+  output (both sides rounded to bf16; against the unrounded fp64 value the
+  bf16 rounding alone is ~1.1e-3 rms);
+* invariants: reruns are bitwise equal; out-of-range ids drop pairs.
+Workloads: small banks (ragged sizes, scales in the SwiGLU's curved region),
+the 64-expert decode layer at full size, and the 256-expert prefill layer at
+full size with sampled tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gemm_mxfp4_dequant_amd import inputs
+from tests.helpers import assert_within, bf16_to_f64, dev, host, ulp_bf16, ulp_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    from gemm_mxfp4_dequant_amd import mxfp4
+    mxfp4.lib()
+    return mxfp4
+
+
+def upload(c):
+    return {k: dev(v) for k, v in c.items()}
+
+
+def silu_d(g):
+    s = 1.0 / (1.0 + np.exp(-np.clip(g, -700, 700)))
+    return s * (1.0 + g * (1.0 - s))
+
+
+def silu(g):
+    return g / (1.0 + np.exp(-np.clip(g, -700, 700)))
+
+
+def gpu_stages(m, d, E, H, I, xbf):
+    """h (slot order) from the stages entry, and the grouping."""
+    T, K = d["ids"].shape
+    offs, pos, slot = m.moe_route_group(d["ids"], E)
+    h = torch.empty((T * K, I), dtype=torch.bfloat16 if xbf else torch.float32, device="cuda")
+    m.moe_experts_mxfp4_stages(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"], d["w"],
+                               out=None, h_out=h)
+    torch.cuda.synchronize()
+    return host(h), host(offs), host(pos), host(slot)
+
+
+def check_case(m, orc, c, E, H, I, xbf, sample_pairs=None, e2e=True):
+    T, K = c["ids"].shape
+    P = T * K
+    d = upload(c)
+    h_gpu, offs, pos, slot = gpu_stages(m, d, E, H, I, xbf)
+    # grouping is exact
+    counts, offs_o, pos_o, slot_o = orc.group(c["ids"], E)
+    assert np.array_equal(offs, offs_o)
+    assert np.array_equal(slot, slot_o)
+    n_valid = int(offs_o[-1])
+    assert np.array_equal(pos[:n_valid], pos_o)
+
+    ids_s = c["ids"].copy().reshape(-1)
+    if sample_pairs is not None:
+        keep = np.zeros(P, bool)
+        keep[sample_pairs] = True
+        ids_s[~keep] = -1
+    ids_s = ids_s.reshape(T, K)
+    st = orc.moe_gate_up(c["gate"], c["up"], E, H, I, c["x"], ids_s, xbf)
+    flat = ids_s.reshape(-1)
+    valid = np.where((flat >= 0) & (flat < E))[0]
+    hp = h_gpu[slot[valid]]
+    hp = bf16_to_f64(hp) if xbf else hp.astype(np.float64)
+    g, u = st["g"][valid], st["u"][valid]
+    tol_extra = 4 * ulp_f32(st["h"][valid]) + (ulp_bf16(st["h"][valid]) if xbf else 0)
+    mag_h = np.abs(silu_d(g)) * np.abs(u) * st["mag_g"][valid] + np.abs(silu(g)) * st["mag_u"][valid]
+    assert_within(hp, st["h"][valid], mag_h, extra=tol_extra, what="h")
+
+    # down + combine fed with the device h
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    h_in = dev(h_gpu)
+    m.moe_experts_mxfp4_stages(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"], d["w"],
+                               out=out, h_in=h_in)
+    out_g = bf16_to_f64(host(out))
+    h_pair = np.zeros((P, I))
+    vv = np.where(slot >= 0)[0]
+    h_pair[vv] = (bf16_to_f64(h_gpu[slot[vv]]) if xbf else h_gpu[slot[vv]].astype(np.float64))
+    tok = np.unique(valid // K) if sample_pairs is not None else np.arange(T)
+    ids_t = np.full_like(c["ids"], -1)
+    ids_t[tok] = c["ids"][tok]
+    y, mag_y = orc.moe_down(c["down"], E, H, I, h_pair, ids_t)
+    o, mag_o = orc.moe_combine(y, mag_y, c["w"], ids_t, E)
+    assert_within(out_g[tok], o[tok], mag_o[tok], extra=ulp_bf16(o[tok]), what="down+combine")
+
+    if e2e:
+        out2 = m.moe_experts_mxfp4(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"], d["w"])
+        out2 = bf16_to_f64(host(out2))
+        ids_e = np.full_like(c["ids"], -1)
+        ids_e[tok] = c["ids"][tok]
+        # both sides rounded to bf16 (the oracle once, from fp64)
+        ref = orc.moe(c["gate"], c["up"], c["down"], E, H, I, c["x"], ids_e, c["w"], xbf)
+        ref = bf16_to_f64(ref["out_bf16"])[tok]
+        got = out2[tok]
+        nrmse = np.sqrt(np.mean((got - ref) ** 2)) / np.sqrt(np.mean(ref ** 2))
+        cos = float((got * ref).sum() / np.sqrt((got * got).sum() * (ref * ref).sum()))
+        assert nrmse < 1e-3 and cos > 0.9999, (nrmse, cos)
+        return out2
+
+
+@pytest.mark.parametrize("xd", ["f32", "bf16"])
+@pytest.mark.parametrize("E,H,I,T,K", [(5, 64, 96, 4, 2), (8, 512, 256, 9, 3), (16, 1024, 512, 20, 4),
+                                       (3, 96, 160, 1, 3), (33, 2048, 1024, 6, 6)])
+def test_small_banks(m, orc, xd, E, H, I, T, K):
+    c = inputs.moe_case(E * 100 + T, E, H, I, T, K, xd, "softmax", scale_lo=100, scale_hi=114)
+    check_case(m, orc, c, E, H, I, xd == "bf16")
+
+
+def test_saturated_scales(m, orc):
+    c = inputs.moe_case(41, 8, 512, 256, 6, 2, "f32", "softmax", scale_lo=118, scale_hi=132)
+    check_case(m, orc, c, 8, 512, 256, False)
+
+
+def test_dropped_ids(m, orc):
+    c = inputs.moe_case(42, 8, 512, 256, 5, 3, "f32", "softmax", scale_lo=100, scale_hi=114)
+    c["ids"] = c["ids"].copy()
+    c["ids"][1, 2] = -1
+    c["ids"][3, 0] = 99
+    check_case(m, orc, c, 8, 512, 256, False)
+
+
+def test_zipf_many_tokens(m, orc):
+    """A hot expert with more tokens than one work item holds."""
+    rng = inputs.rng_for(43)
+    E, H, I, T, K = 16, 512, 256, 200, 4
+    c = inputs.moe_case(43, E, H, I, T, K, "bf16", "zipf", scale_lo=100, scale_hi=114)
+    assert np.bincount(c["ids"].reshape(-1), minlength=E).max() > 40
+    check_case(m, orc, c, E, H, I, True)
+    assert rng is not None
+
+
+def test_workload4_decode_full(m, orc):
+    c = inputs.workload_case(4)
+    cfg = inputs.WORKLOADS[4]
+    check_case(m, orc, c, cfg["n_experts"], cfg["hidden"], cfg["inter"], False)
+
+
+def test_workload5_prefill_sampled(m, orc):
+    cfg = inputs.WORKLOADS[5]
+    c = inputs.workload_case(5)
+    T, K = c["ids"].shape
+    rng = np.random.default_rng(5)
+    toks = rng.choice(T, 3, replace=False)
+    pairs = np.concatenate([t * K + np.arange(K) for t in toks])
+    check_case(m, orc, c, cfg["n_experts"], cfg["hidden"], cfg["inter"], True,
+               sample_pairs=pairs)
+
+
+def test_rerun_bitwise(m):
+    E, H, I, T, K = 16, 1024, 512, 12, 4
+    c = inputs.moe_case(44, E, H, I, T, K, "f32", "softmax", scale_lo=100, scale_hi=114)
+    d = upload(c)
+    o1 = host(m.moe_experts_mxfp4(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"], d["w"]))
+    o2 = host(m.moe_experts_mxfp4(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"], d["w"]))
+    assert np.array_equal(o1, o2)
+
+
+def test_group_large(m, orc):
+    rng = np.random.default_rng(45)
+    for (T, K, E) in [(512, 8, 256), (3000, 4, 1024), (1, 1, 1), (7, 32, 40)]:
+        ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+        offs, pos, slot = m.moe_route_group(dev(ids), E)
+        counts, offs_o, pos_o, slot_o = orc.group(ids, E)
+        assert np.array_equal(host(offs), offs_o)
+        assert np.array_equal(host(pos), pos_o)
+        assert np.array_equal(host(slot), slot_o)
