@@ -1,0 +1,342 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 dequantize-and-multiply path on one MI355X.
+
+Headline step (the metric's workload: a 4096 x 4096 MXFP4 weight, fp32
+activations): one decode matvec (b = 1) and one small-batch GEMM (b = 8),
+each on a different copy of the weight taken from a rotating pool of more
+than 512 MiB, so every launch streams its weight from HBM rather than from
+the 256 MB Infinity Cache.  ``value`` is weight bytes streamed per second
+over exactly --steps steps (wall clock between two device synchronisations,
+inputs resident in HBM).  Launches are replayed from HIP graphs captured on
+torch's stream (the library is stream-ordered and allocation-free), so host
+launch overhead does not hide the kernels.
+
+Also reported (``extra``): each workload's kernel time, weight GB/s and
+fraction of the 8 TB/s peak (256 x 512; 4096 x 4096 at b = 1, 8;
+14336 x 4096 at b = 1..32), the two expert-bank layers in tokens/s (64
+experts decode, 256 experts Zipf prefill), the roofline of the dominant
+kernel, and the CPU oracle timed on a bounded sample of the headline step.
+
+One GPU only: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP4 expert matvec weight GB/s (% of HBM peak) at 1/8 tokens; MoE layer tok/s"
+PEAK_HBM = 8.0e12  # bytes/s, MI355X HBM3E
+POOL_BYTES = 512 * 2 ** 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["device.h", "launch.h", "skinny.hip", "dequant.hip", "route.hip", "api.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gemm_mxfp4_dequant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def tensor_bytes(rows, cols):
+    return rows * cols // 2 + rows * cols // 32
+
+
+class Timer:
+    """Graph-replayed launches timed with HIP events on torch's stream."""
+
+    def __init__(self, torch, launches, eager=False):
+        self.torch = torch
+        self.launches = launches  # list of zero-arg callables (one launch each)
+        self.eager = eager
+        self.graph = None
+        for f in launches:  # warm: attributes set, code loaded
+            f()
+        torch.cuda.synchronize()
+        if not eager:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for f in launches:
+                    f()
+            self.graph = g
+            g.replay()
+            torch.cuda.synchronize()
+
+    def run(self, reps):
+        for _ in range(reps):
+            if self.graph is not None:
+                self.graph.replay()
+            else:
+                for f in self.launches:
+                    f()
+
+    def time(self, reps):
+        """Average GPU ms per launch over ``reps`` passes."""
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        self.run(reps)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(self.launches))
+
+
+def gemm_setup(torch, mx, inputs, rows, cols, b, seed, pool_bytes=POOL_BYTES):
+    nb = tensor_bytes(rows, cols)
+    n = max(2, math.ceil(pool_bytes / nb) + 1)
+    pool = inputs.draw_weights_device(seed, rows, cols, 118, 132, n)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 1000)
+    x = torch.randn((b, cols), generator=g, device="cuda", dtype=torch.float32)
+    y = torch.empty((b, rows), device="cuda", dtype=torch.float32)
+    launches = [lambda i=i: mx.mxfp4_gemm(pool[i], rows, cols, x, b=b, y=y) for i in range(n)]
+    return dict(pool=pool, x=x, y=y, n=n, nb=nb, launches=launches,
+                alg_bytes=nb + b * cols * 4 + b * rows * 4)
+
+
+def moe_setup(torch, mx, inputs, wl, banks):
+    import numpy as np
+    cfg = inputs.WORKLOADS[wl]
+    E, H, I, T, K = (cfg["n_experts"], cfg["hidden"], cfg["inter"], cfg["n_tokens"],
+                     cfg["top_k"])
+    rng = inputs.rng_for(wl)
+    if cfg["routing"] == "softmax":
+        ids, w = inputs.route_softmax(rng, T, E, K)
+    else:
+        ids, w = inputs.route_zipf(rng, T, E, K, cfg["zipf_s"])
+    tb = tensor_bytes(I, H)
+    bank = []
+    for j in range(banks):
+        s = 100 * wl + 10 * j
+        bank.append([inputs.draw_weights_device(s + r, I if r < 2 else H, H if r < 2 else I,
+                                                cfg["scale_lo"], cfg["scale_hi"], E)
+                     for r in range(3)])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl)
+    xdt = torch.float32 if cfg["x_dtype"] == "f32" else torch.bfloat16
+    x = torch.randn((T, H), generator=g, device="cuda", dtype=torch.float32).to(xdt)
+    ids_d = torch.from_numpy(ids).cuda()
+    w_d = torch.from_numpy(w).cuda()
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.moe_experts_mxfp4_workspace_size(T, K, E, H, I, xdt), dtype=torch.uint8,
+                     device="cuda")
+    active = int(np.unique(ids).size)
+    launches = [lambda bk=bk: mx.moe_experts_mxfp4(bk[0], bk[1], bk[2], E, H, I, x, ids_d, w_d,
+                                                   out=out, workspace=ws) for bk in bank]
+    return dict(launches=launches, T=T, touched=active * 3 * tb, active=active, bank=bank,
+                x=x, ids=ids_d, w=w_d, out=out, ws=ws)
+
+
+def cpu_baseline(seconds):
+    """The oracle, as it stands, on the headline step: 4096 x 4096 with b = 1
+    and b = 8 (repeated until ``seconds`` of CPU time have elapsed)."""
+    import oracle
+    from gemm_mxfp4_dequant_amd import inputs
+    w, x = inputs.gemm_case(2, 4096, 4096, 9)
+    threads = oracle.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemm(w, 4096, 4096, x[:1], threads)
+        oracle.gemm(w, 4096, 4096, x[1:9], threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    gbs = reps * 2 * tensor_bytes(4096, 4096) / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} headline steps (4096x4096 fp64 oracle, b=1 and b=8) in "
+                      f"{el:.1f} s", "seconds": round(el, 2)}
+
+
+def load_traffic(key, launches_bytes):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash() or key not in t.get("per_launch", {}):
+        return None
+    e = t["per_launch"][key]
+    return e.get("fetch_bytes", 0) + e.get("write_bytes", 0)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--quick", action="store_true",
+                    help="headline step only (no extra workloads, no CPU baseline)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch eagerly instead of replaying graphs (counter runs)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run plain 1 GiB device copies (counter calibration)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 6 GB prefill layer")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path.  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gemm_mxfp4_dequant_amd import inputs
+    from gemm_mxfp4_dequant_amd import mxfp4 as mx
+
+    if not os.path.exists(mx.LIB_PATH):
+        from gemm_mxfp4_dequant_amd import build as hb
+        hb.build()
+    torch.cuda.set_device(0)
+    mx.lib()
+
+    # ---------------- headline step: 4096^2 at b = 1 and b = 8 -------------
+    rows = cols = 4096
+    s1 = gemm_setup(torch, mx, inputs, rows, cols, 1, 21)
+    s8 = gemm_setup(torch, mx, inputs, rows, cols, 8, 22)
+    n = min(s1["n"], s8["n"])
+    step_launches = []
+    for i in range(n):
+        step_launches += [s1["launches"][i], s8["launches"][i]]
+    G = n  # steps per graph
+    main_t = Timer(torch, step_launches, args.eager)
+    rem = args.steps % G
+    rem_t = Timer(torch, step_launches[: 2 * rem], args.eager) if rem else None
+    warm_reps = max(1, math.ceil(args.warmup / G))
+    main_t.run(warm_reps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    main_t.run(args.steps // G)
+    if rem_t:
+        rem_t.run(1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_bytes = s1["nb"] + s8["nb"]
+    value = args.steps * step_bytes / wall / 1e9
+    log(f"headline: {args.steps} steps in {wall * 1e3:.2f} ms -> {value:.1f} GB/s weight "
+        f"({value / 80:.1f}% of 8 TB/s)")
+
+    # per-kernel launch times (HIP events on the launch stream)
+    k1 = Timer(torch, s1["launches"], args.eager)
+    k8 = Timer(torch, s8["launches"], args.eager)
+    reps = max(3, 4000 // n)
+    ms1, ms8 = k1.time(reps), k8.time(reps)
+    extra = {
+        "gemm_4096x4096_b1": {"us": round(ms1 * 1e3, 3),
+                              "weight_GBps": round(s1["nb"] / ms1 / 1e6, 1),
+                              "pct_peak": round(100 * s1["nb"] / ms1 / 1e6 / 8000, 1)},
+        "gemm_4096x4096_b8": {"us": round(ms8 * 1e3, 3),
+                              "weight_GBps": round(s8["nb"] / ms8 / 1e6, 1),
+                              "pct_peak": round(100 * s8["nb"] / ms8 / 1e6 / 8000, 1)},
+    }
+    for k, v in extra.items():
+        log(f"{k}: {v}")
+    dom, dms, dset = ("gemm_4096x4096_b8", ms8, s8) if ms8 >= ms1 else ("gemm_4096x4096_b1", ms1, s1)
+    achieved = dset["alg_bytes"] / (dms * 1e-3) / 1e9
+    traffic = load_traffic(dom, dset["alg_bytes"])
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": 8000.0,
+                "unit": "GB/s", "frac": round(achieved / 8000.0, 4), "traffic": traffic,
+                "alg_bytes_per_launch": dset["alg_bytes"], "avg_launch_us": round(dms * 1e3, 3)}
+
+    if args.calib_copy:
+        src = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    cpu = None
+    if not args.quick:
+        del main_t, rem_t, k1, k8, s1, s8
+        # 256 x 512 (latency-bound; reported in us)
+        s = gemm_setup(torch, mx, inputs, 256, 512, 1, 1, pool_bytes=0)
+        t = Timer(torch, s["launches"] * 50, args.eager)
+        ms = t.time(20)
+        extra["gemm_256x512_b1"] = {"us": round(ms * 1e3, 3)}
+        log(f"gemm_256x512_b1: {extra['gemm_256x512_b1']}")
+        del s, t
+        for b in (1, 2, 4, 8, 16, 32):
+            s = gemm_setup(torch, mx, inputs, 14336, 4096, b, 30 + b)
+            t = Timer(torch, s["launches"], args.eager)
+            ms = t.time(max(3, 1000 // s["n"]))
+            gb = s["nb"] / ms / 1e6
+            extra[f"gemm_14336x4096_b{b}"] = {"us": round(ms * 1e3, 3),
+                                              "weight_GBps": round(gb, 1),
+                                              "pct_peak": round(100 * gb / 8000, 1)}
+            log(f"gemm_14336x4096_b{b}: {extra[f'gemm_14336x4096_b{b}']}")
+            del s, t
+        torch.cuda.empty_cache()
+        # expert bank, decode layer (2 banks alternate: 466 MB touched per step)
+        s = moe_setup(torch, mx, inputs, 4, 2)
+        t = Timer(torch, s["launches"], args.eager)
+        ms = t.time(100)
+        extra["moe_decode_e64"] = {"us_per_layer": round(ms * 1e3, 2),
+                                   "tok_per_s": round(s["T"] / (ms * 1e-3), 1),
+                                   "touched_GB": round(s["touched"] / 1e9, 4),
+                                   "active_experts": s["active"],
+                                   "touched_GBps": round(s["touched"] / ms / 1e6, 1),
+                                   "pct_peak": round(100 * s["touched"] / ms / 1e6 / 8000, 1)}
+        log(f"moe_decode_e64: {extra['moe_decode_e64']}")
+        del s, t
+        torch.cuda.empty_cache()
+        if not args.no_prefill:
+            s = moe_setup(torch, mx, inputs, 5, 1)
+            t = Timer(torch, s["launches"], args.eager)
+            ms = t.time(5)
+            extra["moe_prefill_e256"] = {"us_per_layer": round(ms * 1e3, 2),
+                                         "tok_per_s": round(s["T"] / (ms * 1e-3), 1),
+                                         "touched_GB": round(s["touched"] / 1e9, 4),
+                                         "active_experts": s["active"],
+                                         "touched_GBps": round(s["touched"] / ms / 1e6, 1),
+                                         "pct_peak": round(100 * s["touched"] / ms / 1e6 / 8000,
+                                                           1)}
+            log(f"moe_prefill_e256: {extra['moe_prefill_e256']}")
+            del s, t
+            torch.cuda.empty_cache()
+        cpu = cpu_baseline(args.cpu_seconds)
+        log(f"cpu_baseline: {cpu}")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "mxfp4 4096x4096 decode matvec b=1 + GEMM b=8, fp32 in/out, "
+                               "cold HBM (rotating >512 MiB weight pool)",
+                   "rows": rows, "cols": cols, "batches": [1, 8], "pool_copies": n,
+                   "launch": "hip graph replay"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

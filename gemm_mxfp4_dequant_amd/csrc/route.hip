@@ -14,6 +14,8 @@
 // k = 0..top_k-1, and the un-permutation of "rlx-cpu 0.2.17,
 // src/gguf_matmul.rs" (grouped_moe_unpermute_out); bf16 output is rounded
 // to nearest-even (the mxg_bf16 rule).
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 
@@ -146,11 +148,14 @@ hipError_t group_launch(const GroupArgs &g, hipStream_t stream)
     size_t lds = ((size_t)nch * g.n_experts + g.n_experts + 2 * GT) * 4;
     if (g.n_pairs <= IDS_IN_LDS)
         lds += (size_t)g.n_pairs * 4;
-    if (lds > 64 * 1024) {
+    static std::atomic<uint8_t> opted{0};
+    if (lds > 64 * 1024 && !opted.load(std::memory_order_acquire)) {
         hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void *>(group_kernel),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            160 * 1024);
         if (st != hipSuccess)
             return st;
+        opted.store(1, std::memory_order_release);
     }
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(GT), lds, stream, g, nch);
     return hipGetLastError();
@@ -159,10 +164,10 @@ hipError_t group_launch(const GroupArgs &g, hipStream_t stream)
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float *y, const int32_t *slot_of_pair,
                                                       const float *w, int top_k, int hidden,
-                                                      void *out)
+                                                      int blocks_per_token, void *out)
 {
-    const int t = blockIdx.y;
-    const int r = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int t = blockIdx.x / blocks_per_token;
+    const int r = ((blockIdx.x % blocks_per_token) * 256 + threadIdx.x) * 4;
     if (r >= hidden)
         return;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -190,13 +195,14 @@ hipError_t combine_launch(const float *y, const int32_t *slot_of_pair, const flo
                           int n_tokens, int top_k, int hidden, void *out, bool out_bf16,
                           hipStream_t stream)
 {
-    dim3 grid((hidden / 4 + 255) / 256, n_tokens);
+    const int bpt = (hidden / 4 + 255) / 256;
+    dim3 grid((unsigned)((int64_t)bpt * n_tokens));
     if (out_bf16)
         hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream, y, slot_of_pair, w,
-                           top_k, hidden, out);
+                           top_k, hidden, bpt, out);
     else
         hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, stream, y, slot_of_pair, w,
-                           top_k, hidden, out);
+                           top_k, hidden, bpt, out);
     return hipGetLastError();
 }
 

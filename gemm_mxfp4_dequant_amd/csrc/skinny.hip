@@ -29,6 +29,8 @@
 //  * The hi and lo columns of a token are summed with one DPP row rotate.
 //  * Each token's column is computed by the same instructions whatever the
 //    other columns hold, so a batch equals its tokens' matvecs bit for bit.
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 
@@ -551,11 +553,18 @@ hipError_t skinny_launch(int mode, bool xbf, int tpc, const SkinnyArgs &a, dim3 
     }
     if (!e)
         return hipErrorInvalidValue;
-    if (lds > 64 * 1024) {
+    // Opt in to more than 64 KB of LDS once per kernel (the largest request
+    // a kernel ever makes is its 160 KB bound), so that later launches,
+    // including ones under graph capture, make no attribute calls.
+    static std::atomic<uint8_t> opted[sizeof(kTable) / sizeof(kTable[0])];
+    std::atomic<uint8_t> &flag = opted[e - kTable];
+    if (lds > 64 * 1024 && !flag.load(std::memory_order_acquire)) {
         hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void *>(e->fn),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            160 * 1024);
         if (st != hipSuccess)
             return st;
+        flag.store(1, std::memory_order_release);
     }
     hipLaunchKernelGGL(e->fn, grid, dim3(NW_GEMM * 64), lds, stream, a);
     return hipGetLastError();

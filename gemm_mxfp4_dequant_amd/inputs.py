@@ -149,3 +149,22 @@ def workload_case(n: int, seed: int | None = None, b: int | None = None):
     return moe_case(seed, cfg["n_experts"], cfg["hidden"], cfg["inter"], cfg["n_tokens"],
                     cfg["top_k"], cfg["x_dtype"], cfg["routing"], cfg.get("zipf_s", 1.1),
                     cfg["scale_lo"], cfg["scale_hi"])
+
+
+def draw_weights_device(seed: int, rows: int, cols: int, scale_lo: int, scale_hi: int,
+                        count: int, device="cuda"):
+    """``count`` stored tensors drawn on the device with a seeded torch
+    generator (same distributions as ``draw_weights``; used for the large
+    rotating pools of the benchmark).  Returns a uint8 tensor [count, bytes]."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    code_bytes = rows * cols // 2
+    n_scales = rows * (cols // 32)
+    out = torch.empty((count, code_bytes + n_scales), dtype=torch.uint8, device=device)
+    for i in range(count):
+        out[i, :code_bytes] = torch.randint(0, 256, (code_bytes,), generator=g, device=device,
+                                            dtype=torch.uint8)
+        out[i, code_bytes:] = torch.randint(scale_lo, scale_hi + 1, (n_scales,), generator=g,
+                                            device=device, dtype=torch.uint8)
+    return out
