@@ -189,8 +189,10 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run plain 1 GiB device copies (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-prefill", action="store_true", help="skip the 6 GB prefill layer")
+    ap.add_argument("--sections", default="gemm,decode,prefill,cpu",
+                    help="extra sections to run: gemm, decode, prefill, cpu")
     args = ap.parse_args()
+    sections = set(args.sections.split(",")) if not args.quick else set()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
@@ -264,8 +266,8 @@ def main():
         del src, dst
 
     cpu = None
-    if not args.quick:
-        del main_t, rem_t, k1, k8, s1, s8
+    del main_t, rem_t, k1, k8, s1, s8
+    if "gemm" in sections:
         # 256 x 512 (latency-bound; reported in us)
         s = gemm_setup(torch, mx, inputs, 256, 512, 1, 1, pool_bytes=0)
         t = Timer(torch, s["launches"] * 50, args.eager)
@@ -284,6 +286,7 @@ def main():
             log(f"gemm_14336x4096_b{b}: {extra[f'gemm_14336x4096_b{b}']}")
             del s, t
         torch.cuda.empty_cache()
+    if "decode" in sections:
         # expert bank, decode layer (2 banks alternate: 466 MB touched per step)
         s = moe_setup(torch, mx, inputs, 4, 2)
         t = Timer(torch, s["launches"], args.eager)
@@ -297,7 +300,8 @@ def main():
         log(f"moe_decode_e64: {extra['moe_decode_e64']}")
         del s, t
         torch.cuda.empty_cache()
-        if not args.no_prefill:
+    if "prefill" in sections:
+        if True:
             s = moe_setup(torch, mx, inputs, 5, 1)
             t = Timer(torch, s["launches"], args.eager)
             ms = t.time(5)
@@ -311,6 +315,7 @@ def main():
             log(f"moe_prefill_e256: {extra['moe_prefill_e256']}")
             del s, t
             torch.cuda.empty_cache()
+    if "cpu" in sections:
         cpu = cpu_baseline(args.cpu_seconds)
         log(f"cpu_baseline: {cpu}")
 

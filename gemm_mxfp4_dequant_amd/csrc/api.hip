@@ -145,9 +145,9 @@ int check_moe(const void *gate, const void *up, const void *down, int64_t n_expe
     if (workspace_bytes < need)
         return fail(MXFP4_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
     const int64_t P = n_tokens * top_k;
-    const int64_t nrb = (hidden + 63) / 64;
+    const int64_t nrb = ((hidden > inter ? hidden : inter) + 15) / 16; // smallest row block
     if (P * nrb > ((int64_t)1 << 31) - 1)
-        return fail(MXFP4_EINVAL, "n_tokens * top_k * hidden/64 too large for one launch");
+        return fail(MXFP4_EINVAL, "n_tokens * top_k * rows/16 too large for one launch");
     return MXFP4_OK;
 }
 
@@ -207,9 +207,11 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
         a.work = work;
         a.n_work = n_work;
         a.token_of_slot = tos;
-        const int nrb = (int)((inter + mx::skinny_rows_per_wg(mx::MODE_GATEUP) - 1) /
-                              mx::skinny_rows_per_wg(mx::MODE_GATEUP));
-        TRY(launched(mx::skinny_launch(mx::MODE_GATEUP, xbf, tpc, a, dim3(nrb * max_work), st),
+        const mx::SkinnyShape sh =
+            mx::skinny_shape(mx::MODE_GATEUP, xbf, (int)inter, (int)hidden, tpc, max_work);
+        const int64_t nrb = (inter + sh.rows_per_wg - 1) / sh.rows_per_wg;
+        TRY(launched(mx::skinny_launch(mx::MODE_GATEUP, xbf, sh, a, (unsigned)(nrb * max_work),
+                                       st),
                      "gate/up"));
         if (h_out)
             TRY(launched(mx::copy_launch(h_out, h, (size_t)P * inter * (xbf ? 2 : 4), st),
@@ -229,9 +231,10 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
         a.y_bf16 = 0;
         a.work = work;
         a.n_work = n_work;
-        const int nrb = (int)((hidden + mx::skinny_rows_per_wg(mx::MODE_DOWN) - 1) /
-                              mx::skinny_rows_per_wg(mx::MODE_DOWN));
-        TRY(launched(mx::skinny_launch(mx::MODE_DOWN, xbf, tpc, a, dim3(nrb * max_work), st),
+        const mx::SkinnyShape sh =
+            mx::skinny_shape(mx::MODE_DOWN, xbf, (int)hidden, (int)inter, tpc, max_work);
+        const int64_t nrb = (hidden + sh.rows_per_wg - 1) / sh.rows_per_wg;
+        TRY(launched(mx::skinny_launch(mx::MODE_DOWN, xbf, sh, a, (unsigned)(nrb * max_work), st),
                      "down"));
     }
     TRY(launched(mx::combine_launch(y, slot, topk_w, (int)n_tokens, (int)top_k, (int)hidden, out,
@@ -282,8 +285,8 @@ int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_d
         return fail(MXFP4_EINVAL, "cols = %lld too large for the on-chip operand buffers",
                     (long long)cols);
     const int64_t nch = (b + tpc - 1) / tpc;
-    const int rw = mx::skinny_rows_per_wg(mx::MODE_GEMM);
-    const int64_t nrb = (rows + rw - 1) / rw;
+    const mx::SkinnyShape sh = mx::skinny_shape(mx::MODE_GEMM, xbf, (int)rows, (int)cols, tpc, nch);
+    const int64_t nrb = (rows + sh.rows_per_wg - 1) / sh.rows_per_wg;
     if (nch * nrb > ((int64_t)1 << 31) - 1)
         return fail(MXFP4_EINVAL, "rows * b too large for one launch");
     mx::SkinnyArgs a = {};
@@ -295,7 +298,7 @@ int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_d
     a.nch = (int)nch;
     a.y = y;
     a.y_bf16 = y_dtype == MXFP4_BF16;
-    return launched(mx::skinny_launch(mx::MODE_GEMM, xbf, tpc, a, dim3((unsigned)(nch * nrb)),
+    return launched(mx::skinny_launch(mx::MODE_GEMM, xbf, sh, a, (unsigned)(nch * nrb),
                                       (hipStream_t)stream),
                     "gemm");
 }

@@ -25,12 +25,19 @@ struct SkinnyArgs {
     const int *token_of_slot; // GATEUP: token row of each slot
 };
 
-int skinny_rows_per_wg(int mode);
+// Launch shape of one skinny call: K slab width (0 = generic kernel),
+// tokens per workgroup, row tiles per matrix, threads, LDS bytes.
+struct SkinnyShape {
+    int kw, tpc, nr, threads, rows_per_wg;
+    size_t lds;
+};
+
 // Tokens per workgroup for a call that wants `want` columns (fits LDS).
 int skinny_pick_tpc(int mode, bool xbf, int cols, int want);
-size_t skinny_lds_bytes(int mode, bool xbf, int cols, int tpc);
-hipError_t skinny_launch(int mode, bool xbf, int tpc, const SkinnyArgs &a, dim3 grid,
-                         hipStream_t stream);
+// Shape for `items` token chunks / work items per row block.
+SkinnyShape skinny_shape(int mode, bool xbf, int rows, int cols, int tpc, int64_t items);
+hipError_t skinny_launch(int mode, bool xbf, const SkinnyShape &s, const SkinnyArgs &a,
+                         unsigned blocks, hipStream_t stream);
 
 hipError_t dequant_launch(const uint8_t *w, int64_t rows, int64_t cols, void *out, bool bf16,
                           hipStream_t stream);

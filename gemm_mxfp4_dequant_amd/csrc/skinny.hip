@@ -8,12 +8,11 @@
 // src/qtensor/moe_fast.rs": gate_up_block, down_block).
 //
 // How (MI355X design, not the pages' workgroup-per-row shader):
-//  * A workgroup owns a block of output rows and all of K.  Its waves split
-//    the rows: each wave owns 16 rows (one MFMA tile) and streams them with
-//    128-bit loads, a lane loading one whole 32-column group (16 bytes) of
-//    one row per load step.  All of a wave's K blocks are in flight at once
-//    (or a ring of PF blocks for long rows), so every lane keeps several KB
-//    of HBM traffic outstanding.
+//  * A workgroup owns NR tiles of 16 output rows (per matrix) and all of K.
+//    Its waves form a grid: row tile x K slab.  A wave streams its 16 rows
+//    over one slab of KW columns with 128-bit loads, a lane loading one
+//    whole 32-column group (16 bytes) of one row per load step; all of a
+//    wave's loads are issued before it waits for any of them.
 //  * The E8M0 scales of the workgroup's rows are staged in LDS with
 //    coalesced 16-byte loads, once per workgroup.
 //  * The activations of the (up to TPC) tokens are staged in LDS once per
@@ -22,14 +21,20 @@
 //    and occupy two MFMA columns each; bf16 activations occupy one.
 //  * Each group is decoded once per workgroup by v_cvt_scalef32_pk_bf16_fp4
 //    straight into the MFMA A operand (exact: E2M1 times a power of two is a
-//    bf16), and fed to v_mfma_f32_16x16x32_bf16, which does the K reduction
+//    bf16) and fed to v_mfma_f32_16x16x32_bf16, which does the K reduction
 //    of the dot products (the pages' LDS reduction tree is not needed).
 //    MFMA step (L, m) pairs lane slice s with group 4L+s, elements 8m..8m+7;
 //    a dot product is order-free, so this k-order follows the 128-bit load.
-//  * The hi and lo columns of a token are summed with one DPP row rotate.
+//    Two accumulators alternate so consecutive MFMAs do not wait on each
+//    other.
+//  * The K slabs of a row tile are summed in LDS in slab order, and the hi
+//    and lo columns of a token with one DPP row rotate.
 //  * Each token's column is computed by the same instructions whatever the
 //    other columns hold, so a batch equals its tokens' matvecs bit for bit.
+#include <algorithm>
 #include <atomic>
+#include <climits>
+#include <mutex>
 
 #include "device.h"
 #include "launch.h"
@@ -38,24 +43,22 @@ namespace mx {
 
 namespace {
 
-constexpr int KB = 512;       // columns per K block
-constexpr int LPB = KB / 128; // 128-column load steps per block
-constexpr int BPAD = 8;       // bf16 padding per LDS operand row (bank spread)
+constexpr int BPAD = 8; // bf16 padding per LDS operand row (bank spread)
 
 struct TileMap {
-    int ntok;     // valid token columns of this workgroup
-    int slot0;    // first token (GEMM) / first slot (MoE)
-    int row0;     // first output row
-    int expert;   // MoE expert (0 for GEMM)
+    int ntok;   // valid token columns of this workgroup
+    int slot0;  // first token (GEMM) / first slot (MoE)
+    int row0;   // first output row
+    int expert; // MoE expert (0 for GEMM)
 };
 
-// Work item of this workgroup; returns false if it has none (MoE grids are
-// sized by an upper bound).
+// Work item of this workgroup; false if it has none (MoE grids are sized by
+// an upper bound).  Flattened grid, item/chunk fastest: consecutive
+// workgroups share row blocks, so a row block's weights are reused from L2
+// across chunks.
 template <int MODE, int TPC>
 __device__ __forceinline__ bool tile_map(const SkinnyArgs &a, int rows_wg, TileMap &m)
 {
-    // Flattened grid, item/chunk fastest: consecutive workgroups share row
-    // blocks, so a row block's weights are reused from L2 across chunks.
     const int sub = blockIdx.x % a.nch;
     m.row0 = (blockIdx.x / a.nch) * rows_wg;
     if (MODE == MODE_GEMM) {
@@ -65,10 +68,9 @@ __device__ __forceinline__ bool tile_map(const SkinnyArgs &a, int rows_wg, TileM
         m.expert = 0;
         return true;
     }
-    const int item = sub;
-    if (item >= *a.n_work)
+    if (sub >= *a.n_work)
         return false;
-    const int4 wk = reinterpret_cast<const int4 *>(a.work)[item];
+    const int4 wk = reinterpret_cast<const int4 *>(a.work)[sub];
     m.expert = wk.x;
     m.slot0 = wk.y;
     m.ntok = wk.z;
@@ -84,251 +86,240 @@ __device__ __forceinline__ int64_t token_row(const SkinnyArgs &a, int slot0, int
     return slot0 + t;
 }
 
-// LDS row of the B operand read by lane column j (hi rows 0..ntok-1, lo
-// rows ntok..2ntok-1 for fp32; rows 0..ntok-1 for bf16), or -1 for a zero
-// column.
+// LDS operand row read by lane column j: hi rows 0..ntok-1 and lo rows
+// ntok..2ntok-1 for fp32, rows 0..ntok-1 for bf16.  A column without a
+// token reads row 0: its MFMA column is never stored, and MFMA columns do
+// not mix.
 template <bool XBF>
 __device__ __forceinline__ int b_row(int j, int ntok)
 {
     if (XBF)
-        return j < ntok ? j : -1;
+        return j < ntok ? j : 0;
     if (j < 8)
-        return j < ntok ? j : -1;
-    return (j - 8) < ntok ? ntok + (j - 8) : -1;
+        return j < ntok ? j : 0;
+    return (j - 8) < ntok ? ntok + (j - 8) : 0;
 }
 
-// Epilogue: the wave's 16x16 accumulator tile -> outputs.
-// acc[i] = D[4*ls + i][li].  For fp32 inputs the lo column li+8 is folded
-// into column li.
+// Load the 8 activation elements of unit (t, seg) into v (bf16: 4 words).
 template <int MODE, bool XBF>
-__device__ __forceinline__ void epilogue(const SkinnyArgs &a, const TileMap &tm, f32x4 acc,
-                                         int mat, int tile, int lane, float *xch)
+__device__ __forceinline__ void load_unit(const SkinnyArgs &a, int slot0, int t, int seg, int C,
+                                          float *v)
+{
+    const int64_t row = token_row<MODE>(a, slot0, t);
+    if (XBF) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(
+            reinterpret_cast<const uint16_t *>(a.x) + row * C + seg * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = __uint_as_float(w[i]);
+    } else {
+        const float *xr = reinterpret_cast<const float *>(a.x) + row * C + seg * 8;
+        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(xr);
+        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(xr + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = v0[i];
+            v[4 + i] = v1[i];
+        }
+    }
+}
+
+// Write unit (t, seg) to the LDS operand rows (fp32: split into hi and lo).
+template <bool XBF>
+__device__ __forceinline__ void store_unit(__bf16 *Bs, int bstride, int ntok, int t, int seg,
+                                           const float *v)
+{
+    if (XBF) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = __float_as_uint(v[i]);
+        *reinterpret_cast<u32x4 *>(Bs + t * bstride + seg * 8) = w;
+    } else {
+        bf16x8 hi, lo;
+        split_bf16x8(v, hi, lo);
+        *reinterpret_cast<bf16x8 *>(Bs + t * bstride + seg * 8) = hi;
+        *reinterpret_cast<bf16x8 *>(Bs + (ntok + t) * bstride + seg * 8) = lo;
+    }
+}
+
+// Final tile -> outputs.  g[i] = D[4*ls + i][li] of the (gate) tile, u the
+// up tile (GATEUP only).  For fp32 inputs the lo column li+8 is folded into
+// column li first.
+template <int MODE, bool XBF>
+__device__ __forceinline__ void store_tile(const SkinnyArgs &a, const TileMap &tm, f32x4 g,
+                                           f32x4 u, int tile, int lane)
 {
     const int li = lane & 15, ls = lane >> 4;
     if (!XBF) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc[i] += dpp_row_ror8(acc[i]);
+        for (int i = 0; i < 4; ++i) {
+            g[i] += dpp_row_ror8(g[i]);
+            if (MODE == MODE_GATEUP)
+                u[i] += dpp_row_ror8(u[i]);
+        }
     }
     const bool col_ok = XBF ? (li < tm.ntok) : (li < 8 && li < tm.ntok);
-    const int R = a.rows;
-    const int rbase = tm.row0 + tile * 16 + 4 * ls;
-
-    if (MODE == MODE_GATEUP) {
-        // up waves hand their tile to the gate waves through LDS
-        if (mat == 1) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xch[(tile * 64 + lane) * 4 + i] = acc[i];
-        }
-        __syncthreads();
-        if (mat == 1 || !col_ok)
-            return;
-        const int64_t slot = tm.slot0 + li;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rbase + i;
-            if (r >= R)
-                continue;
-            const float u = xch[(tile * 64 + lane) * 4 + i];
-            const float h = silu(acc[i]) * u;
-            if (a.y_bf16)
-                reinterpret_cast<uint16_t *>(a.y)[slot * R + r] = f32_to_bf16_bits(h);
-            else
-                reinterpret_cast<float *>(a.y)[slot * R + r] = h;
-        }
-        return;
-    }
     if (!col_ok)
         return;
-    const int64_t orow = tm.slot0 + li; // token (GEMM) or slot (DOWN)
+    const int R = a.rows;
+    const int rbase = tm.row0 + tile * 16 + 4 * ls;
+    const int64_t orow = tm.slot0 + li; // token (GEMM) or slot (MoE)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = rbase + i;
         if (r >= R)
             continue;
-        if (MODE == MODE_GEMM && a.y_bf16)
-            reinterpret_cast<uint16_t *>(a.y)[orow * R + r] = f32_to_bf16_bits(acc[i]);
+        float v = g[i];
+        if (MODE == MODE_GATEUP)
+            v = silu(g[i]) * u[i];
+        if (MODE != MODE_DOWN && a.y_bf16)
+            reinterpret_cast<uint16_t *>(a.y)[orow * R + r] = f32_to_bf16_bits(v);
         else
-            reinterpret_cast<float *>(a.y)[orow * R + r] = acc[i];
+            reinterpret_cast<float *>(a.y)[orow * R + r] = v;
     }
 }
 
 } // namespace
 
-// Static-K kernel: cols == NKB * 512.
-template <int NW, int NKB, int PF, int TPC, bool XBF, int MODE>
-__global__ __launch_bounds__(NW * 64) void skinny_static(SkinnyArgs a)
+// Split-K kernel: cols % KW == 0.  blockDim = nwr * (cols / KW) * 64.
+template <int KW, int TPC, bool XBF, int MODE, int MAXW>
+__global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
 {
-    constexpr int NT = NW * 64;
-    constexpr int COLS = NKB * KB;
-    constexpr int GPR = COLS / 32;
-    constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
-    constexpr int TILES = (MODE == MODE_GATEUP) ? NW / 2 : NW;
-    constexpr int ROWS_WG = TILES * 16;
+    constexpr int LS = KW / 128; // load steps per wave
     constexpr int NBC = XBF ? TPC : 2 * TPC;
-    constexpr int BSTRIDE = COLS + BPAD;
-    constexpr int SSTRIDE = GPR + 16;
-    constexpr int SEGS = COLS / 8;                   // 8-element segments per row
-    constexpr int SPT = (SEGS + NT - 1) / NT;        // segments per thread per token
-    constexpr int SCHUNK = GPR / 16;                 // 16-byte scale chunks per row
-    constexpr int SUNITS = NMAT * ROWS_WG * SCHUNK;
-    constexpr int SUPT = (SUNITS + NT - 1) / NT;
-    static_assert(PF >= 1 && PF <= NKB, "ring depth");
+    // activation units (8 elements) per thread issued up front: enough for
+    // one row tile per matrix (units <= TPC * cols / 8, threads >= cols / KW * 64)
+    constexpr int UMAX = TPC * KW / 512 < 1 ? 1 : (TPC * KW / 512 > 8 ? 8 : TPC * KW / 512);
+    constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
+    const int C = a.cols;
+    const int gpr = C / 32;
+    const int nwk = C / KW;
+    const int NT = blockDim.x;
+    const int nwr = NT / 64 / nwk;
+    const int NR = nwr / NMAT;
+    const int rows_wg = NR * 16;
+    const int bstride = C + BPAD;
+    const int sstride = gpr + 16;
 
     extern __shared__ __align__(16) uint8_t smem[];
     __bf16 *Bs = reinterpret_cast<__bf16 *>(smem);
-    uint8_t *Ss = smem + NBC * BSTRIDE * 2;
-    float *xch = reinterpret_cast<float *>(Ss + NMAT * ROWS_WG * SSTRIDE);
+    const int bbytes = max(NBC * bstride * 2, nwr * nwk * 1024);
+    uint8_t *Ss = smem + ((bbytes + 15) & ~15);
+    f32x4 *red = reinterpret_cast<f32x4 *>(smem); // reuses the operand rows
 
     TileMap tm;
-    if (!tile_map<MODE, TPC>(a, ROWS_WG, tm))
+    if (!tile_map<MODE, TPC>(a, rows_wg, tm))
         return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / nwk, wk = wave % nwk;
+    const int mat = wr / NR, tile = wr % NR;
     const int li = lane & 15, ls = lane >> 4;
     const int R = a.rows;
     const uint8_t *A0 = a.w0 + (int64_t)tm.expert * a.expert_stride;
     const uint8_t *A1 = (MODE == MODE_GATEUP) ? a.w1 + (int64_t)tm.expert * a.expert_stride : A0;
-    const int64_t code_bytes = (int64_t)R * (COLS / 2);
+    const int64_t code_bytes = (int64_t)R * (C / 2);
 
-    // ---- 1. issue activation and scale loads (older than the weight loads,
-    //         so waiting for them does not wait for HBM)
-    float xv[TPC][SPT][8];
+    // ---- 1. activation and scale loads, issued before the weight loads so
+    //         that waiting for them does not wait for HBM
+    const int segs = C / 8;
+    const int units = tm.ntok * segs;
+    float xv[UMAX][8];
 #pragma unroll
-    for (int t = 0; t < TPC; ++t) {
-        if (t < tm.ntok) {
-            const float *xr = nullptr;
-            const uint16_t *xb = nullptr;
-            const int64_t row = token_row<MODE>(a, tm.slot0, t);
-            if (XBF)
-                xb = reinterpret_cast<const uint16_t *>(a.x) + row * COLS;
-            else
-                xr = reinterpret_cast<const float *>(a.x) + row * COLS;
-#pragma unroll
-            for (int q = 0; q < SPT; ++q) {
-                const int seg = tid + q * NT;
-                if (SEGS % NT == 0 || seg < SEGS) {
-                    if (XBF) {
-                        const u32x4 v = *reinterpret_cast<const u32x4 *>(xb + seg * 8);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            xv[t][q][i] = __uint_as_float(v[i]);
-                    } else {
-                        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(xr + seg * 8);
-                        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(xr + seg * 8 + 4);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            xv[t][q][i] = v0[i];
-                            xv[t][q][4 + i] = v1[i];
-                        }
-                    }
-                }
-            }
-        }
-    }
-    u32x4 sv[SUPT];
-#pragma unroll
-    for (int q = 0; q < SUPT; ++q) {
+    for (int q = 0; q < UMAX; ++q) {
         const int u = tid + q * NT;
-        sv[q] = u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
-        if (SUNITS % NT == 0 || u < SUNITS) {
-            const int mat = u / (ROWS_WG * SCHUNK);
-            const int rr = (u / SCHUNK) % ROWS_WG;
-            const int ch = u % SCHUNK;
-            const int r = tm.row0 + rr;
-            if (r < R) {
-                const uint8_t *base = (mat ? A1 : A0) + code_bytes + (int64_t)r * GPR + ch * 16;
-                sv[q] = *reinterpret_cast<const u32x4 *>(base);
-            }
+        if (u < units) {
+            const int t = u / segs;
+            load_unit<MODE, XBF>(a, tm.slot0, t, u - t * segs, C, xv[q]);
         }
     }
-
-    // ---- 2. issue this wave's weight stream (ring of PF blocks)
-    const int mat = (MODE == MODE_GATEUP) ? wave / TILES : 0;
-    const int tile = (MODE == MODE_GATEUP) ? wave % TILES : wave;
-    const int r = tm.row0 + tile * 16 + li;
-    const bool rvalid = r < R;
-    const uint8_t *arow = (mat ? A1 : A0) + (int64_t)(rvalid ? r : 0) * (COLS / 2) + ls * 16;
-    u32x4 ring[PF][LPB];
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-#pragma unroll
-        for (int L = 0; L < LPB; ++L)
-            ring[p][L] = rvalid ? *reinterpret_cast<const u32x4 *>(arow + p * 256 + L * 64)
-                                : u32x4{0, 0, 0, 0};
-
-    // ---- 3. activations -> LDS operands; scales -> LDS
-#pragma unroll
-    for (int t = 0; t < TPC; ++t) {
-        if (t < tm.ntok) {
-#pragma unroll
-            for (int q = 0; q < SPT; ++q) {
-                const int seg = tid + q * NT;
-                if (SEGS % NT == 0 || seg < SEGS) {
-                    if (XBF) {
-                        u32x4 v;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            v[i] = __float_as_uint(xv[t][q][i]);
-                        *reinterpret_cast<u32x4 *>(Bs + t * BSTRIDE + seg * 8) = v;
-                    } else {
-                        bf16x8 hi, lo;
-                        split_bf16x8(xv[t][q], hi, lo);
-                        *reinterpret_cast<bf16x8 *>(Bs + t * BSTRIDE + seg * 8) = hi;
-                        *reinterpret_cast<bf16x8 *>(Bs + (tm.ntok + t) * BSTRIDE + seg * 8) = lo;
-                    }
-                }
-            }
-        }
+    const int sch = gpr / 16;                // 16-byte scale chunks per row
+    const int sunits = NMAT * rows_wg * sch; // <= NT
+    u32x4 sv = {0, 0, 0, 0};
+    int srr = 0, sc16 = 0;
+    if (tid < sunits) {
+        const int m = tid / (rows_wg * sch);
+        srr = tid / sch; // m * rows_wg + row
+        sc16 = tid % sch;
+        // rows past the end read row R-1: their outputs are never stored, and
+        // an MFMA output row depends on its own A row only
+        const int r = min(tm.row0 + srr - m * rows_wg, R - 1);
+        sv = *reinterpret_cast<const u32x4 *>((m ? A1 : A0) + code_bytes + (int64_t)r * gpr +
+                                               sc16 * 16);
     }
+
+    // ---- 2. this wave's weight loads
+    const int r = min(tm.row0 + tile * 16 + li, R - 1);
+    const uint8_t *arow = (mat ? A1 : A0) + (int64_t)r * (C / 2) + wk * (KW / 2) + ls * 16;
+    u32x4 cw[LS];
 #pragma unroll
-    for (int q = 0; q < SUPT; ++q) {
+    for (int L = 0; L < LS; ++L)
+        cw[L] = *reinterpret_cast<const u32x4 *>(arow + L * 64);
+
+    // ---- 3. activations and scales -> LDS
+#pragma unroll
+    for (int q = 0; q < UMAX; ++q) {
         const int u = tid + q * NT;
-        if (SUNITS % NT == 0 || u < SUNITS) {
-            const int rr = u / SCHUNK; // mat * ROWS_WG + row
-            const int ch = u % SCHUNK;
-            *reinterpret_cast<u32x4 *>(Ss + rr * SSTRIDE + ch * 16) = sv[q];
+        if (u < units) {
+            const int t = u / segs;
+            store_unit<XBF>(Bs, bstride, tm.ntok, t, u - t * segs, xv[q]);
         }
     }
+    for (int u = tid + UMAX * NT; u < units; u += NT) { // beyond the up-front batch
+        float v[8];
+        const int t = u / segs;
+        load_unit<MODE, XBF>(a, tm.slot0, t, u - t * segs, C, v);
+        store_unit<XBF>(Bs, bstride, tm.ntok, t, u - t * segs, v);
+    }
+    if (tid < sunits)
+        *reinterpret_cast<u32x4 *>(Ss + srr * sstride + sc16 * 16) = sv;
     __syncthreads();
 
-    // ---- 4. decode + MFMA over K
-    const int brow = b_row<XBF>(li, tm.ntok);
-    const __bf16 *bb = Bs + (brow < 0 ? 0 : brow) * BSTRIDE + ls * 32;
-    const uint8_t *srow = Ss + (mat * ROWS_WG + tile * 16 + li) * SSTRIDE;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const bf16x8 zero8 = {};
+    // ---- 4. decode + MFMA over this wave's slab
+    const __bf16 *bb = Bs + b_row<XBF>(li, tm.ntok) * bstride + wk * KW + ls * 32;
+    const uint8_t *srow = Ss + (mat * rows_wg + tile * 16 + li) * sstride + wk * (KW / 32);
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-        const int slot = kb % PF;
-        const u32x4 sc = *reinterpret_cast<const u32x4 *>(srow + kb * 16);
+    for (int L = 0; L < LS; ++L) {
+        const float scf = e8m0_operand_of(*reinterpret_cast<const uint32_t *>(srow + 4 * L), ls);
+        bf16x8 bv[4];
 #pragma unroll
-        for (int L = 0; L < LPB; ++L) {
-            const float scf = e8m0_operand_of(sc[L], ls);
-            const u32x4 cw = ring[slot][L];
+        for (int m = 0; m < 4; ++m)
+            bv[m] = *reinterpret_cast<const bf16x8 *>(bb + L * 128 + m * 8);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const bf16x8 av = decode8_bf16(cw[m], scf);
-                const bf16x8 bv = brow >= 0
-                    ? *reinterpret_cast<const bf16x8 *>(bb + kb * KB + L * 128 + m * 8)
-                    : zero8;
-                acc = mfma16x16x32(av, bv, acc);
-            }
-        }
-        if (kb + PF < NKB) {
-#pragma unroll
-            for (int L = 0; L < LPB; ++L)
-                ring[slot][L] = rvalid
-                    ? *reinterpret_cast<const u32x4 *>(arow + (kb + PF) * 256 + L * 64)
-                    : u32x4{0, 0, 0, 0};
+        for (int m = 0; m < 4; ++m) {
+            const bf16x8 av = decode8_bf16(cw[L][m], scf);
+            if (m & 1)
+                acc1 = mfma16x16x32(av, bv[m], acc1);
+            else
+                acc0 = mfma16x16x32(av, bv[m], acc0);
         }
     }
+    const f32x4 part = acc0 + acc1;
 
-    epilogue<MODE, XBF>(a, tm, acc, mat, tile, lane, xch);
+    // ---- 5. sum the K slabs in order, then store
+    __syncthreads(); // every wave is done with the operand rows
+    red[(wr * nwk + wk) * 64 + lane] = part;
+    __syncthreads();
+    if (wk != 0 || mat != 0)
+        return;
+    f32x4 g = red[(wr * nwk) * 64 + lane];
+    for (int k = 1; k < nwk; ++k)
+        g += red[(wr * nwk + k) * 64 + lane];
+    f32x4 u = g;
+    if (MODE == MODE_GATEUP) {
+        const int wu = NR + tile;
+        u = red[(wu * nwk) * 64 + lane];
+        for (int k = 1; k < nwk; ++k)
+            u += red[(wu * nwk + k) * 64 + lane];
+    }
+    store_tile<MODE, XBF>(a, tm, g, u, tile, lane);
 }
 
-// Generic kernel: any cols % 32 == 0 (K steps of 128 columns, guarded).
+// Generic kernel: any cols % 32 == 0 (K steps of 128 columns, guarded, one
+// wave per row tile).  Used for column counts the split-K kernel does not
+// take.
 template <int NW, int TPC, bool XBF, int MODE>
 __global__ __launch_bounds__(NW * 64) void skinny_generic(SkinnyArgs a)
 {
@@ -370,7 +361,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_generic(SkinnyArgs a)
                 float xvv = 0.f;
                 if (c + i < C) {
                     if (XBF)
-                        xvv = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a.x)[row * C + c + i]);
+                        xvv = bf16_bits_to_f32(
+                            reinterpret_cast<const uint16_t *>(a.x)[row * C + c + i]);
                     else
                         xvv = reinterpret_cast<const float *>(a.x)[row * C + c + i];
                 }
@@ -395,134 +387,138 @@ __global__ __launch_bounds__(NW * 64) void skinny_generic(SkinnyArgs a)
         const int m = u / (ROWS_WG * gpr);
         const int rr = (u / gpr) % ROWS_WG;
         const int g = u % gpr;
-        const int r = tm.row0 + rr;
-        uint8_t k = 127;
-        if (r < R)
-            k = ((m ? A1 : A0) + code_bytes)[(int64_t)r * gpr + g];
-        Ss[(m * ROWS_WG + rr) * sstride + g] = k;
+        const int r = min(tm.row0 + rr, R - 1);
+        Ss[(m * ROWS_WG + rr) * sstride + g] = ((m ? A1 : A0) + code_bytes)[(int64_t)r * gpr + g];
     }
     __syncthreads();
 
     const int mat = (MODE == MODE_GATEUP) ? wave / TILES : 0;
     const int tile = (MODE == MODE_GATEUP) ? wave % TILES : wave;
-    const int r = tm.row0 + tile * 16 + li;
-    const bool rvalid = r < R;
-    const uint8_t *arow = (mat ? A1 : A0) + (int64_t)(rvalid ? r : 0) * (C / 2);
+    const int r = min(tm.row0 + tile * 16 + li, R - 1);
+    const uint8_t *arow = (mat ? A1 : A0) + (int64_t)r * (C / 2);
     const uint8_t *srow = Ss + (mat * ROWS_WG + tile * 16 + li) * sstride;
-    const int brow = b_row<XBF>(li, tm.ntok);
-    const __bf16 *bb = Bs + (brow < 0 ? 0 : brow) * bstride + ls * 32;
-    const bf16x8 zero8 = {};
+    const __bf16 *bb = Bs + b_row<XBF>(li, tm.ntok) * bstride + ls * 32;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int nsteps = cpad / 128;
     for (int st = 0; st < nsteps; ++st) {
         const int g = st * 4 + ls;
         u32x4 cw = {0, 0, 0, 0};
         uint32_t k = 127;
-        if (rvalid && g < gpr) {
+        if (g < gpr) {
             cw = *reinterpret_cast<const u32x4 *>(arow + (int64_t)g * 16);
             k = srow[g];
         }
         const float scf = e8m0_operand(k);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const bf16x8 av = decode8_bf16(cw[m], scf);
-            const bf16x8 bv = brow >= 0 ? *reinterpret_cast<const bf16x8 *>(bb + st * 128 + m * 8)
-                                        : zero8;
-            acc = mfma16x16x32(av, bv, acc);
+            const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(bb + st * 128 + m * 8);
+            acc = mfma16x16x32(decode8_bf16(cw[m], scf), bv, acc);
         }
     }
-    epilogue<MODE, XBF>(a, tm, acc, mat, tile, lane, xch);
+    if (MODE == MODE_GATEUP) {
+        // up waves hand their tile to the gate waves through LDS
+        if (mat == 1)
+            reinterpret_cast<f32x4 *>(xch)[tile * 64 + lane] = acc;
+        __syncthreads();
+        if (mat == 1)
+            return;
+        store_tile<MODE, XBF>(a, tm, acc, reinterpret_cast<f32x4 *>(xch)[tile * 64 + lane], tile,
+                              lane);
+        return;
+    }
+    store_tile<MODE, XBF>(a, tm, acc, acc, tile, lane);
 }
 
 // ---------------------------------------------------------------------------
-// Host side: instantiation table and launch
+// Host side: instantiation table, launch shape and launch
 // ---------------------------------------------------------------------------
 
 namespace {
 
-constexpr int NW_GEMM = 4;
-
-size_t lds_static(int nkb, int tpc, bool xbf, int mode)
-{
-    const int cols = nkb * KB;
-    const int nmat = mode == MODE_GATEUP ? 2 : 1;
-    const int tiles = mode == MODE_GATEUP ? NW_GEMM / 2 : NW_GEMM;
-    const int nbc = xbf ? tpc : 2 * tpc;
-    size_t b = (size_t)nbc * (cols + BPAD) * 2;
-    b += (size_t)nmat * tiles * 16 * (cols / 32 + 16);
-    if (mode == MODE_GATEUP)
-        b += (size_t)tiles * 64 * 4 * 4;
-    return b;
-}
-
-size_t lds_generic(int cols, int tpc, bool xbf, int mode)
-{
-    const int nmat = mode == MODE_GATEUP ? 2 : 1;
-    const int tiles = mode == MODE_GATEUP ? NW_GEMM / 2 : NW_GEMM;
-    const int nbc = xbf ? tpc : 2 * tpc;
-    const int cpad = (cols + 127) / 128 * 128;
-    const int gpr = cols / 32;
-    size_t b = (size_t)nbc * (cpad + BPAD) * 2;
-    b += (size_t)nmat * tiles * 16 * ((gpr + 15) / 16 * 16 + 16);
-    if (mode == MODE_GATEUP)
-        b += (size_t)tiles * 64 * 4 * 4;
-    return b;
-}
+constexpr int NW_GENERIC = 4;
+constexpr int LDS_MAX = 160 * 1024;
 
 typedef void (*KernelFn)(SkinnyArgs);
 
 struct Entry {
-    int mode, xbf, nkb, tpc; // nkb 0 = generic
+    int mode, xbf, kw, tpc, maxw; // kw 0 = generic
     KernelFn fn;
 };
 
-#define MX_S(MODE, XBF, NKB, PF, TPC) \
-    {MODE, XBF, NKB, TPC, skinny_static<NW_GEMM, NKB, PF, TPC, (bool)XBF, MODE>}
-#define MX_G(MODE, XBF, TPC) {MODE, XBF, 0, TPC, skinny_generic<NW_GEMM, TPC, (bool)XBF, MODE>}
-
-#define MX_FP32_SET(MODE, NKB, PF) \
-    MX_S(MODE, 0, NKB, PF, 1), MX_S(MODE, 0, NKB, PF, 2), MX_S(MODE, 0, NKB, PF, 4), \
-    MX_S(MODE, 0, NKB, PF, 8)
-#define MX_BF16_SET(MODE, NKB, PF) \
-    MX_S(MODE, 1, NKB, PF, 2), MX_S(MODE, 1, NKB, PF, 4), MX_S(MODE, 1, NKB, PF, 8), \
-    MX_S(MODE, 1, NKB, PF, 16)
-#define MX_GEN_SET(MODE) \
+#define MX_K(MODE, XBF, KW, TPC, MAXW) \
+    {MODE, XBF, KW, TPC, MAXW, skinny_splitk<KW, TPC, (bool)XBF, MODE, MAXW>}
+#define MX_KW(MODE, XBF, KW, TPC) MX_K(MODE, XBF, KW, TPC, 8), MX_K(MODE, XBF, KW, TPC, 16)
+#define MX_F32(MODE, KW) \
+    MX_KW(MODE, 0, KW, 1), MX_KW(MODE, 0, KW, 2), MX_KW(MODE, 0, KW, 4), MX_KW(MODE, 0, KW, 8)
+#define MX_B16(MODE, KW) \
+    MX_KW(MODE, 1, KW, 2), MX_KW(MODE, 1, KW, 4), MX_KW(MODE, 1, KW, 8), MX_KW(MODE, 1, KW, 16)
+#define MX_G(MODE, XBF, TPC) \
+    {MODE, XBF, 0, TPC, NW_GENERIC, skinny_generic<NW_GENERIC, TPC, (bool)XBF, MODE>}
+#define MX_GEN(MODE) \
     MX_G(MODE, 0, 1), MX_G(MODE, 0, 2), MX_G(MODE, 0, 4), MX_G(MODE, 0, 8), MX_G(MODE, 1, 2), \
-    MX_G(MODE, 1, 4), MX_G(MODE, 1, 8), MX_G(MODE, 1, 16)
+        MX_G(MODE, 1, 4), MX_G(MODE, 1, 8), MX_G(MODE, 1, 16)
+#define MX_MODE(MODE) \
+    MX_F32(MODE, 512), MX_F32(MODE, 1024), MX_B16(MODE, 512), MX_B16(MODE, 1024), MX_GEN(MODE)
 
-const Entry kTable[] = {
-    MX_FP32_SET(MODE_GEMM, 1, 1), MX_FP32_SET(MODE_GEMM, 4, 4), MX_FP32_SET(MODE_GEMM, 8, 8),
-    MX_BF16_SET(MODE_GEMM, 1, 1), MX_BF16_SET(MODE_GEMM, 4, 4), MX_BF16_SET(MODE_GEMM, 8, 8),
-    MX_FP32_SET(MODE_GATEUP, 8, 8), MX_FP32_SET(MODE_GATEUP, 4, 4),
-    MX_BF16_SET(MODE_GATEUP, 8, 8), MX_S(MODE_GATEUP, 1, 14, 7, 2),
-    MX_S(MODE_GATEUP, 1, 14, 7, 4), MX_S(MODE_GATEUP, 1, 14, 7, 8),
-    MX_FP32_SET(MODE_DOWN, 4, 4), MX_FP32_SET(MODE_DOWN, 8, 8), MX_BF16_SET(MODE_DOWN, 4, 4),
-    MX_GEN_SET(MODE_GEMM), MX_GEN_SET(MODE_GATEUP), MX_GEN_SET(MODE_DOWN),
-};
+const Entry kTable[] = {MX_MODE(MODE_GEMM), MX_MODE(MODE_GATEUP), MX_MODE(MODE_DOWN)};
+constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
-const Entry *find(int mode, int xbf, int nkb, int tpc)
+const Entry *find(int mode, bool xbf, int kw, int tpc, int maxw)
 {
     for (const Entry &e : kTable)
-        if (e.mode == mode && e.xbf == xbf && e.nkb == nkb && e.tpc == tpc)
+        if (e.mode == mode && e.xbf == (int)xbf && e.kw == kw && e.tpc == tpc &&
+            (kw == 0 || e.maxw == maxw))
             return &e;
     return nullptr;
 }
 
-} // namespace
+int nmat(int mode) { return mode == MODE_GATEUP ? 2 : 1; }
 
-int skinny_rows_per_wg(int mode) { return mode == MODE_GATEUP ? NW_GEMM / 2 * 16 : NW_GEMM * 16; }
+size_t lds_splitk(int mode, bool xbf, int cols, int kw, int tpc, int nr)
+{
+    const int nbc = xbf ? tpc : 2 * tpc;
+    const int nwr = nr * nmat(mode);
+    const size_t bbytes =
+        std::max((size_t)nbc * (cols + BPAD) * 2, (size_t)nwr * (cols / kw) * 1024);
+    return ((bbytes + 15) & ~(size_t)15) + (size_t)nwr * 16 * (cols / 32 + 16);
+}
+
+size_t lds_generic(int mode, bool xbf, int cols, int tpc)
+{
+    const int tiles = mode == MODE_GATEUP ? NW_GENERIC / 2 : NW_GENERIC;
+    const int nbc = xbf ? tpc : 2 * tpc;
+    const int cpad = (cols + 127) / 128 * 128;
+    const int gpr = cols / 32;
+    size_t b = (size_t)nbc * (cpad + BPAD) * 2;
+    b += (size_t)nmat(mode) * tiles * 16 * ((gpr + 15) / 16 * 16 + 16);
+    if (mode == MODE_GATEUP)
+        b += (size_t)tiles * 64 * 16;
+    return b;
+}
+
+// K slab width for the split-K kernel (0: use the generic kernel).
+int pick_kw(int mode, int cols)
+{
+    for (int kw : {512, 1024})
+        if (cols % kw == 0 && (cols / kw) * nmat(mode) <= 16)
+            return kw;
+    return 0;
+}
+
+} // namespace
 
 int skinny_pick_tpc(int mode, bool xbf, int cols, int want)
 {
     static const int f32_opts[] = {1, 2, 4, 8};
     static const int b16_opts[] = {2, 4, 8, 16};
     const int *opts = xbf ? b16_opts : f32_opts;
+    const int kw = pick_kw(mode, cols);
     int best = 0;
     for (int i = 0; i < 4; ++i) {
         const int t = opts[i];
-        const bool fits = (cols % KB == 0 ? lds_static(cols / KB, t, xbf, mode)
-                                          : lds_generic(cols, t, xbf, mode)) <= 160 * 1024;
-        if (!fits)
+        const size_t lds =
+            kw ? lds_splitk(mode, xbf, cols, kw, t, 1) : lds_generic(mode, xbf, cols, t);
+        if (lds > (size_t)LDS_MAX)
             break;
         best = t;
         if (t >= want)
@@ -531,42 +527,96 @@ int skinny_pick_tpc(int mode, bool xbf, int cols, int want)
     return best;
 }
 
-size_t skinny_lds_bytes(int mode, bool xbf, int cols, int tpc)
+namespace {
+
+// Workgroups of this kernel that fit on one CU (registers, LDS, waves), as
+// the runtime computes it; cached per (kernel, threads, LDS).
+int wgs_per_cu(const Entry *e, int threads, size_t lds)
 {
-    const int nkb = cols % KB == 0 ? cols / KB : 0;
-    if (nkb && find(mode, xbf, nkb, tpc))
-        return lds_static(nkb, tpc, xbf, mode);
-    return lds_generic(cols, tpc, xbf, mode);
+    struct Key {
+        const Entry *e;
+        int threads;
+        size_t lds;
+        int n;
+    };
+    static std::mutex mu;
+    static Key cache[128];
+    static int used = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].e == e && cache[i].threads == threads && cache[i].lds == lds)
+            return cache[i].n;
+    int n = 0;
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(e->fn),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, LDS_MAX);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(e->fn),
+                                                     threads, lds) != hipSuccess ||
+        n < 1)
+        n = 1;
+    if (used < 128)
+        cache[used++] = Key{e, threads, lds, n};
+    return n;
 }
 
-hipError_t skinny_launch(int mode, bool xbf, int tpc, const SkinnyArgs &a, dim3 grid,
-                         hipStream_t stream)
+} // namespace
+
+SkinnyShape skinny_shape(int mode, bool xbf, int rows, int cols, int tpc, int64_t items)
 {
-    const int nkb = a.cols % KB == 0 ? a.cols / KB : 0;
-    const Entry *e = nkb ? find(mode, xbf, nkb, tpc) : nullptr;
-    size_t lds;
-    if (e) {
-        lds = lds_static(nkb, tpc, xbf, mode);
-    } else {
-        e = find(mode, xbf, 0, tpc);
-        lds = lds_generic(a.cols, tpc, xbf, mode);
+    SkinnyShape s = {};
+    s.kw = pick_kw(mode, cols);
+    s.tpc = tpc;
+    if (!s.kw) {
+        s.nr = mode == MODE_GATEUP ? NW_GENERIC / 2 : NW_GENERIC;
+        s.threads = NW_GENERIC * 64;
+        s.lds = lds_generic(mode, xbf, cols, tpc);
+        s.rows_per_wg = s.nr * 16;
+        return s;
     }
+    const int nwk = cols / s.kw;
+    const int nr_max = 16 / (nwk * nmat(mode));
+    // Fewest rounds of co-resident workgroups; ties go to more row tiles per
+    // workgroup (less activation staging per row).
+    int64_t best_rounds = INT64_MAX;
+    for (int nr = 1; nr <= nr_max && nr <= 4; nr *= 2) {
+        const size_t lds = lds_splitk(mode, xbf, cols, s.kw, tpc, nr);
+        if (lds > (size_t)LDS_MAX)
+            break;
+        const int threads = nr * nmat(mode) * nwk * 64;
+        const Entry *e = find(mode, xbf, s.kw, tpc, threads <= 512 ? 8 : 16);
+        const int per_cu = e ? wgs_per_cu(e, threads, lds) : 1;
+        const int64_t wgs = (int64_t)((rows + nr * 16 - 1) / (nr * 16)) * items;
+        const int64_t rounds = (wgs + 256LL * per_cu - 1) / (256LL * per_cu);
+        if (rounds <= best_rounds) {
+            best_rounds = rounds;
+            s.nr = nr;
+            s.threads = threads;
+            s.lds = lds;
+        }
+    }
+    s.rows_per_wg = s.nr * 16;
+    return s;
+}
+
+hipError_t skinny_launch(int mode, bool xbf, const SkinnyShape &s, const SkinnyArgs &a,
+                         unsigned blocks, hipStream_t stream)
+{
+    const int waves = s.threads / 64;
+    const Entry *e = find(mode, xbf, s.kw, s.tpc, waves <= 8 ? 8 : 16);
     if (!e)
         return hipErrorInvalidValue;
-    // Opt in to more than 64 KB of LDS once per kernel (the largest request
-    // a kernel ever makes is its 160 KB bound), so that later launches,
-    // including ones under graph capture, make no attribute calls.
-    static std::atomic<uint8_t> opted[sizeof(kTable) / sizeof(kTable[0])];
+    // Opt in to more than 64 KB of LDS once per kernel, so that later
+    // launches (including ones under graph capture) make no attribute calls.
+    static std::atomic<uint8_t> opted[kTableSize];
     std::atomic<uint8_t> &flag = opted[e - kTable];
-    if (lds > 64 * 1024 && !flag.load(std::memory_order_acquire)) {
+    if (s.lds > 64 * 1024 && !flag.load(std::memory_order_acquire)) {
         hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void *>(e->fn),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                            160 * 1024);
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_MAX);
         if (st != hipSuccess)
             return st;
         flag.store(1, std::memory_order_release);
     }
-    hipLaunchKernelGGL(e->fn, grid, dim3(NW_GEMM * 64), lds, stream, a);
+    hipLaunchKernelGGL(e->fn, dim3(blocks), dim3(s.threads), s.lds, stream, a);
     return hipGetLastError();
 }
 
