@@ -58,30 +58,42 @@ def tensor_bytes(rows, cols):
 class Timer:
     """Graph-replayed launches timed with HIP events on torch's stream."""
 
-    def __init__(self, torch, launches, eager=False):
+    def __init__(self, torch, launches, eager=False, passes=None):
         self.torch = torch
         self.launches = launches  # list of zero-arg callables (one launch each)
         self.eager = eager
         self.graph = None
+        self.passes = 1
         for f in launches:  # warm: attributes set, code loaded
             f()
         torch.cuda.synchronize()
         if not eager:
+            # enough passes over the launch list in one graph that replay
+            # boundaries are a small part of the timed span
+            self.passes = passes if passes else max(1, 256 // len(launches))
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for f in launches:
-                    f()
+                for _ in range(self.passes):
+                    for f in launches:
+                        f()
             self.graph = g
             g.replay()
             torch.cuda.synchronize()
 
     def run(self, reps):
-        for _ in range(reps):
-            if self.graph is not None:
+        """``reps`` passes over the launch list."""
+        if self.graph is not None:
+            for _ in range((reps + self.passes - 1) // self.passes):
                 self.graph.replay()
-            else:
+        else:
+            for _ in range(reps):
                 for f in self.launches:
                     f()
+
+    def launches_run(self, reps):
+        if self.graph is not None:
+            return (reps + self.passes - 1) // self.passes * self.passes * len(self.launches)
+        return reps * len(self.launches)
 
     def time(self, reps):
         """Average GPU ms per launch over ``reps`` passes."""
@@ -93,7 +105,7 @@ class Timer:
         self.run(reps)
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * len(self.launches))
+        return e0.elapsed_time(e1) / self.launches_run(reps)
 
 
 def gemm_setup(torch, mx, inputs, rows, cols, b, seed, pool_bytes=POOL_BYTES):
@@ -217,15 +229,18 @@ def main():
     step_launches = []
     for i in range(n):
         step_launches += [s1["launches"][i], s8["launches"][i]]
-    G = n  # steps per graph
+    # exactly --steps steps: whole replays of the multi-pass graph, then one
+    # replay of a graph holding the remaining steps
     main_t = Timer(torch, step_launches, args.eager)
-    rem = args.steps % G
-    rem_t = Timer(torch, step_launches[: 2 * rem], args.eager) if rem else None
-    warm_reps = max(1, math.ceil(args.warmup / G))
-    main_t.run(warm_reps)
+    per_replay = n * main_t.passes if not args.eager else n
+    full, rem = divmod(args.steps, per_replay)
+    rem_launches = [step_launches[i % (2 * n)] for i in range(2 * rem)]
+    rem_t = Timer(torch, rem_launches, args.eager, passes=1) if rem else None
+    main_t.run(max(1, math.ceil(args.warmup / n)))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    main_t.run(args.steps // G)
+    for _ in range(full):
+        main_t.run(per_replay // n)
     if rem_t:
         rem_t.run(1)
     torch.cuda.synchronize()

@@ -43,6 +43,18 @@ int group_max_work(int n_pairs, int n_experts, int tpc)
     return bound < n_pairs ? bound : n_pairs;
 }
 
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d, 64);
+        if (lane >= d)
+            v += o;
+    }
+    return v;
+}
+
 __global__ __launch_bounds__(GT) void group_kernel(GroupArgs g, int nch)
 {
     extern __shared__ __align__(16) int32_t lds[];
@@ -51,7 +63,9 @@ __global__ __launch_bounds__(GT) void group_kernel(GroupArgs g, int nch)
     int32_t *tot = cnt + nch * E;       // [E]
     int32_t *scan_a = tot + E;          // [GT] offsets scan
     int32_t *scan_b = scan_a + GT;      // [GT] work-item scan
-    int32_t *sids = scan_b + GT;        // [P] when P <= IDS_IN_LDS
+    int32_t *wsum_a = scan_b + GT;      // [GT / 64] wave totals
+    int32_t *wsum_b = wsum_a + GT / 64;
+    int32_t *sids = wsum_b + GT / 64;   // [P] when P <= IDS_IN_LDS
     const bool ids_lds = P <= IDS_IN_LDS;
     const int cs = (P + nch - 1) / nch;
 
@@ -84,20 +98,25 @@ __global__ __launch_bounds__(GT) void group_kernel(GroupArgs g, int nch)
         tot[e] = run;
     }
     __syncthreads();
-    // 3. inclusive scans over experts (E <= GT) of counts and work items
+    // 3. inclusive scans over experts (E <= GT) of counts and work items:
+    //    shuffle scans within waves, then the wave totals
     {
         const int n = tid < E ? tot[tid] : 0;
-        scan_a[tid] = n;
-        scan_b[tid] = (n + g.tpc - 1) / g.tpc;
-        __syncthreads();
-        for (int d = 1; d < GT; d <<= 1) {
-            const int a = tid >= d ? scan_a[tid - d] : 0;
-            const int b = tid >= d ? scan_b[tid - d] : 0;
-            __syncthreads();
-            scan_a[tid] += a;
-            scan_b[tid] += b;
-            __syncthreads();
+        int a = wave_inclusive_scan(n);
+        int b = wave_inclusive_scan((n + g.tpc - 1) / g.tpc);
+        const int wave = tid >> 6;
+        if ((tid & 63) == 63) {
+            wsum_a[wave] = a;
+            wsum_b[wave] = b;
         }
+        __syncthreads();
+        for (int w = 0; w < wave; ++w) {
+            a += wsum_a[w];
+            b += wsum_b[w];
+        }
+        scan_a[tid] = a;
+        scan_b[tid] = b;
+        __syncthreads();
     }
     // offsets (exclusive) and the total
     if (tid < E) {
@@ -145,7 +164,7 @@ __global__ __launch_bounds__(GT) void group_kernel(GroupArgs g, int nch)
 hipError_t group_launch(const GroupArgs &g, hipStream_t stream)
 {
     const int nch = group_chunks(g.n_pairs, g.n_experts);
-    size_t lds = ((size_t)nch * g.n_experts + g.n_experts + 2 * GT) * 4;
+    size_t lds = ((size_t)nch * g.n_experts + g.n_experts + 2 * GT + 2 * (GT / 64)) * 4;
     if (g.n_pairs <= IDS_IN_LDS)
         lds += (size_t)g.n_pairs * 4;
     static std::atomic<uint8_t> opted{0};
@@ -171,15 +190,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *y, const int3
     if (r >= hidden)
         return;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < top_k; ++k) {
-        const int s = slot_of_pair[t * top_k + k];
-        if (s < 0)
-            continue;
-        const float wk = w[t * top_k + k];
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(y + (int64_t)s * hidden + r);
+    // slots in groups of 8: all loads of a group are issued before the sums
+    for (int k0 = 0; k0 < top_k; k0 += 8) {
+        f32x4 v[8];
+        float wk[8];
+        bool ok[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc[i] += wk * v[i];
+        for (int j = 0; j < 8; ++j) {
+            const int k = k0 + j;
+            const int s = k < top_k ? slot_of_pair[t * top_k + k] : -1;
+            ok[j] = s >= 0;
+            wk[j] = ok[j] ? w[t * top_k + k] : 0.f;
+            v[j] = ok[j] ? *reinterpret_cast<const f32x4 *>(y + (int64_t)s * hidden + r)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (!ok[j])
+                continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i] += wk[j] * v[j][i];
+        }
     }
     if (OUT_BF16) {
         u32x2 o;

@@ -573,26 +573,48 @@ SkinnyShape skinny_shape(int mode, bool xbf, int rows, int cols, int tpc, int64_
         s.rows_per_wg = s.nr * 16;
         return s;
     }
-    const int nwk = cols / s.kw;
-    const int nr_max = 16 / (nwk * nmat(mode));
-    // Fewest rounds of co-resident workgroups; ties go to more row tiles per
-    // workgroup (less activation staging per row).
-    int64_t best_rounds = INT64_MAX;
-    for (int nr = 1; nr <= nr_max && nr <= 4; nr *= 2) {
-        const size_t lds = lds_splitk(mode, xbf, cols, s.kw, tpc, nr);
-        if (lds > (size_t)LDS_MAX)
-            break;
-        const int threads = nr * nmat(mode) * nwk * 64;
-        const Entry *e = find(mode, xbf, s.kw, tpc, threads <= 512 ? 8 : 16);
-        const int per_cu = e ? wgs_per_cu(e, threads, lds) : 1;
-        const int64_t wgs = (int64_t)((rows + nr * 16 - 1) / (nr * 16)) * items;
-        const int64_t rounds = (wgs + 256LL * per_cu - 1) / (256LL * per_cu);
-        if (rounds <= best_rounds) {
-            best_rounds = rounds;
-            s.nr = nr;
-            s.threads = threads;
-            s.lds = lds;
+    // Candidates: slab width x row tiles.  Measured preference order on
+    // MI355X (cold 8.9 MB and 31 MB weights, b = 1..8): fewest rounds of
+    // co-resident workgroups; then at least 256 workgroups (one per CU);
+    // then 8-wave workgroups; then the fewest workgroups.
+    bool found = false;
+    int64_t bk0 = 0, bk1 = 0, bk2 = 0, bk3 = 0;
+    for (int kw : {512, 1024}) {
+        if (cols % kw != 0)
+            continue;
+        const int nwk = cols / kw;
+        for (int nr = 1; nr <= 4; nr *= 2) {
+            const int waves = nr * nmat(mode) * nwk;
+            if (waves > 16)
+                break;
+            const size_t lds = lds_splitk(mode, xbf, cols, kw, tpc, nr);
+            if (lds > (size_t)LDS_MAX)
+                break;
+            const Entry *e = find(mode, xbf, kw, tpc, waves <= 8 ? 8 : 16);
+            if (!e)
+                continue;
+            const int per_cu = wgs_per_cu(e, waves * 64, lds);
+            const int64_t wgs = (int64_t)((rows + nr * 16 - 1) / (nr * 16)) * items;
+            const int64_t k0 = (wgs + 256LL * per_cu - 1) / (256LL * per_cu);
+            const int64_t k1 = wgs < 256 ? 1 : 0;
+            const int64_t k2 = waves > 8 ? waves - 8 : 8 - waves;
+            const int64_t k3 = wgs < 256 ? -wgs : wgs;
+            if (!found || k0 < bk0 || (k0 == bk0 && (k1 < bk1 || (k1 == bk1 &&
+                (k2 < bk2 || (k2 == bk2 && k3 < bk3)))))) {
+                found = true;
+                bk0 = k0, bk1 = k1, bk2 = k2, bk3 = k3;
+                s.kw = kw;
+                s.nr = nr;
+                s.threads = waves * 64;
+                s.lds = lds;
+            }
         }
+    }
+    if (!found) { // no split-K shape fits: the generic kernel
+        s.kw = 0;
+        s.nr = mode == MODE_GATEUP ? NW_GENERIC / 2 : NW_GENERIC;
+        s.threads = NW_GENERIC * 64;
+        s.lds = lds_generic(mode, xbf, cols, tpc);
     }
     s.rows_per_wg = s.nr * 16;
     return s;
