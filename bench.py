@@ -273,10 +273,13 @@ def main():
                 "alg_bytes_per_launch": dset["alg_bytes"], "avg_launch_us": round(dms * 1e3, 3)}
 
     if args.calib_copy:
-        src = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
+        # a plain elementwise kernel of known traffic for counter calibration:
+        # reads 1 GiB (cold: written before the 1 GiB destination) and
+        # writes 1 GiB
+        src = torch.ones(2 ** 28, dtype=torch.float32, device="cuda")
+        dst = torch.zeros_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
