@@ -14,6 +14,8 @@
 #include "../../include/mxfp4.h"
 #include "launch.h"
 
+#include <cmath>
+
 namespace {
 
 thread_local char g_err[512];
@@ -169,15 +171,19 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
     void *h = ws + L.h;
     float *y = reinterpret_cast<float *>(ws + L.y);
 
-    // tokens per work item: the mean number of pairs per active expert
-    // (measured best on the 64-expert decode layer: a hot expert with more
-    // tokens takes several items, re-reading its rows from L2)
-    const int64_t active = n_experts < P ? n_experts : P;
-    int want = (int)((P + active - 1) / active);
+    // Work items: tokens per item = mean pairs per touched expert, where the
+    // touched count is its expectation under uniform routing,
+    // E * (1 - (1 - 1/E)^P) (64-expert decode: 48 pairs -> 34 experts -> 2
+    // tokens per item, measured best); an expert with more pairs takes
+    // several items, each re-reading its rows (from L2 when they run
+    // together: items of one row block share an XCD).
+    const double touched =
+        (double)n_experts * (1.0 - std::pow(1.0 - 1.0 / (double)n_experts, (double)P));
+    int want = (int)std::ceil((double)P / (touched > 1.0 ? touched : 1.0));
     if (want > 16)
         want = 16;
-    int tpc_gu = mx::skinny_pick_tpc(mx::MODE_GATEUP, xbf, (int)hidden, want);
-    int tpc_dn = mx::skinny_pick_tpc(mx::MODE_DOWN, xbf, (int)inter, want);
+    const int tpc_gu = mx::skinny_pick_tpc(mx::MODE_GATEUP, xbf, (int)hidden, want);
+    const int tpc_dn = mx::skinny_pick_tpc(mx::MODE_DOWN, xbf, (int)inter, want);
     const int tpc = tpc_gu < tpc_dn ? tpc_gu : tpc_dn;
     if (tpc < 1)
         return fail(MXFP4_EINVAL, "hidden/inter too large for the on-chip operand buffers");
@@ -214,10 +220,7 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
         a.token_of_slot = tos;
         const mx::SkinnyShape sh =
             mx::skinny_shape(mx::MODE_GATEUP, xbf, (int)inter, (int)hidden, tpc, max_work);
-        const int64_t nrb = (inter + sh.rows_per_wg - 1) / sh.rows_per_wg;
-        TRY(launched(mx::skinny_launch(mx::MODE_GATEUP, xbf, sh, a, (unsigned)(nrb * max_work),
-                                       st),
-                     "gate/up"));
+        TRY(launched(mx::skinny_launch(mx::MODE_GATEUP, xbf, sh, a, st), "gate/up"));
         if (h_out)
             TRY(launched(mx::copy_launch(h_out, h, (size_t)P * inter * (xbf ? 2 : 4), st),
                          "h copy"));
@@ -238,9 +241,7 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
         a.n_work = n_work;
         const mx::SkinnyShape sh =
             mx::skinny_shape(mx::MODE_DOWN, xbf, (int)hidden, (int)inter, tpc, max_work);
-        const int64_t nrb = (hidden + sh.rows_per_wg - 1) / sh.rows_per_wg;
-        TRY(launched(mx::skinny_launch(mx::MODE_DOWN, xbf, sh, a, (unsigned)(nrb * max_work), st),
-                     "down"));
+        TRY(launched(mx::skinny_launch(mx::MODE_DOWN, xbf, sh, a, st), "down"));
     }
     TRY(launched(mx::combine_launch(y, slot, topk_w, (int)n_tokens, (int)top_k, (int)hidden, out,
                                     out_dtype == MXFP4_BF16, st),
@@ -291,8 +292,7 @@ int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_d
                     (long long)cols);
     const int64_t nch = (b + tpc - 1) / tpc;
     const mx::SkinnyShape sh = mx::skinny_shape(mx::MODE_GEMM, xbf, (int)rows, (int)cols, tpc, nch);
-    const int64_t nrb = (rows + sh.rows_per_wg - 1) / sh.rows_per_wg;
-    if (nch * nrb > ((int64_t)1 << 31) - 1)
+    if (mx::skinny_blocks(sh, (int)rows, (int)nch) > ((int64_t)1 << 31) - 1)
         return fail(MXFP4_EINVAL, "rows * b too large for one launch");
     mx::SkinnyArgs a = {};
     a.w0 = static_cast<const uint8_t *>(w);
@@ -303,9 +303,7 @@ int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_d
     a.nch = (int)nch;
     a.y = y;
     a.y_bf16 = y_dtype == MXFP4_BF16;
-    return launched(mx::skinny_launch(mx::MODE_GEMM, xbf, sh, a, (unsigned)(nch * nrb),
-                                      (hipStream_t)stream),
-                    "gemm");
+    return launched(mx::skinny_launch(mx::MODE_GEMM, xbf, sh, a, (hipStream_t)stream), "gemm");
 }
 
 int mxfp4_matvec(const void *w, int64_t rows, int64_t cols, const float *x, float *y, void *stream)

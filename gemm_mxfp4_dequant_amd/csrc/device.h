@@ -99,4 +99,16 @@ __device__ __forceinline__ float dpp_row_ror8(float v)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+constexpr int NXCD = 8; // MI355X: 8 XCDs, each with its own L2
+
+// Workgroups are dispatched to the XCDs round-robin by id.  This maps the
+// dispatch id to a logical id so that each XCD receives a contiguous range
+// of logical ids (a bijection on [0, n)).
+__device__ __forceinline__ int xcd_logical(int pid, int n)
+{
+    const int x = pid % NXCD, i = pid / NXCD;
+    const int base = n / NXCD, rem = n % NXCD;
+    return x < rem ? x * (base + 1) + i : rem * (base + 1) + (x - rem) * base + i;
+}
+
 } // namespace mx

@@ -17,7 +17,9 @@ struct SkinnyArgs {
     int rows, cols;           // of one tensor
     const void *x;            // GEMM: x [b][cols]; GATEUP: x [T][cols]; DOWN: h [slots][cols]
     int b;                    // GEMM: tokens
-    int nch;                  // grid = row blocks * nch (GEMM: token chunks; MoE: item bound)
+    int nch;                  // GEMM: token chunks; MoE: work item bound
+    int nrb;                  // row blocks of rows_per_wg rows (set by skinny_launch)
+    int rbw;                  // row blocks walked by one workgroup (set by skinny_launch)
     void *y;                  // GEMM: y [b][rows]; GATEUP: h [slots][rows]; DOWN: y [slots][rows]
     int y_bf16;               // output element type (GEMM, GATEUP)
     const int *work;          // MoE: int4 {expert, first slot, tokens, 0} per item
@@ -26,9 +28,10 @@ struct SkinnyArgs {
 };
 
 // Launch shape of one skinny call: K slab width (0 = generic kernel),
-// tokens per workgroup, row tiles per matrix, threads, LDS bytes.
+// tokens per workgroup, row tiles per matrix, threads, row blocks walked by
+// one workgroup, LDS bytes.
 struct SkinnyShape {
-    int kw, tpc, nr, threads, rows_per_wg;
+    int kw, tpc, nr, threads, rows_per_wg, rbw;
     size_t lds;
 };
 
@@ -36,8 +39,10 @@ struct SkinnyShape {
 int skinny_pick_tpc(int mode, bool xbf, int cols, int want);
 // Shape for `items` token chunks / work items per row block.
 SkinnyShape skinny_shape(int mode, bool xbf, int rows, int cols, int tpc, int64_t items);
-hipError_t skinny_launch(int mode, bool xbf, const SkinnyShape &s, const SkinnyArgs &a,
-                         unsigned blocks, hipStream_t stream);
+// Workgroups of a launch: ceil(ceil(rows / rows_per_wg) / rbw) * nch.
+int64_t skinny_blocks(const SkinnyShape &s, int rows, int nch);
+hipError_t skinny_launch(int mode, bool xbf, const SkinnyShape &s, SkinnyArgs a,
+                         hipStream_t stream);
 
 hipError_t dequant_launch(const uint8_t *w, int64_t rows, int64_t cols, void *out, bool bf16,
                           hipStream_t stream);

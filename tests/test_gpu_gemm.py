@@ -93,16 +93,38 @@ def test_wide_scale_range(m, orc):
     check(m, orc, 128, 1024, 4, 11, lo=60, hi=190)
 
 
-@pytest.mark.parametrize("rows,cols", [(300, 2304), (5, 5120), (128, 4096), (64, 7168)])
+def test_many_row_blocks_per_workgroup(m, orc):
+    """Tall, narrow weights with 40 tokens: enough workgroups that each one
+    walks several row blocks (ragged last block)."""
+    check(m, orc, 65553, 512, 40, 31)
+
+
+@pytest.mark.parametrize("rows,cols", [(300, 2304), (5, 5120), (128, 4096), (64, 7168),
+                                       (14336, 4096), (200, 1024), (65553, 512)])
 def test_batch_equals_matvec_bitwise(m, rows, cols):
-    w, x = inputs.gemm_case(rows + cols, rows, cols, 19)
+    """Every token of a batch equals its own matvec bit for bit, for one and
+    several token chunks, with and without row-block walking, and every launch
+    shape: all kernels sum in one canonical order."""
+    w, x = inputs.gemm_case(rows + cols, rows, cols, 40)
     wd = dev(w)
-    for b in (2, 8, 9, 19):
+    for b in (2, 8, 9, 19, 40):
         xb = dev(x[:b])
         yb = host(m.mxfp4_gemm(wd, rows, cols, xb))
         for t in range(b):
             y1 = host(m.mxfp4_matvec(wd, rows, cols, dev(x[t])))
             assert np.array_equal(y1.view(np.uint32), yb[t].view(np.uint32)), (b, t)
+
+
+@pytest.mark.parametrize("rows,cols", [(256, 4096), (96, 2048)])
+def test_bf16_batch_equals_single_bitwise(m, rows, cols):
+    w, x = inputs.gemm_case(rows + 7, rows, cols, 70, x_dtype="bf16")
+    wd = dev(w)
+    xd = dev(x)
+    y1 = [host(m.mxfp4_gemm(wd, rows, cols, xd[t:t + 1])) for t in range(70)]
+    for b in (3, 16, 17, 70):
+        yb = host(m.mxfp4_gemm(wd, rows, cols, xd[:b]))
+        for t in range(b):
+            assert np.array_equal(y1[t][0].view(np.uint32), yb[t].view(np.uint32)), (b, t)
 
 
 def test_permuted_tokens_permute_outputs(m):
