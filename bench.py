@@ -36,7 +36,7 @@ METRIC = "MXFP4 expert matvec weight GB/s (% of HBM peak) at 1/8 tokens; MoE lay
 PEAK_HBM = 8.0e12  # bytes/s, MI355X HBM3E
 POOL_BYTES = 512 * 2 ** 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["device.h", "launch.h", "skinny.hip", "dequant.hip", "route.hip",
+KERNEL_SOURCES = ["device.h", "launch.h", "skinny.hip", "tiled.hip", "dequant.hip", "route.hip",
                   "api.hip"]
 
 

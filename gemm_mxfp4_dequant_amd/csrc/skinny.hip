@@ -28,11 +28,11 @@
 //    MFMA step (L, m) pairs lane slice s with group 4L+s, elements 8m..8m+7;
 //    a dot product is order-free, so this k-order follows the 128-bit load.
 //  * Summation order (the same in every kernel of this library, whatever
-//    the launch shape): K is cut into 512-column units; within a unit two
-//    accumulators alternate by MFMA step (steps m = 0, 2 and m = 1, 3 of each
-//    128 columns), the unit's partial is acc0 + acc1, and the units are
-//    summed in ascending order (through LDS across waves).  The hi and lo
-//    columns of a token are then added with one DPP row rotate.
+//    the launch shape): K is cut into 512-column units; within a unit one
+//    accumulator takes the unit's 16 MFMA steps in k order (MFMA accumulation
+//    into its own destination issues back to back), and the unit partials
+//    are summed in ascending order (through LDS across waves).  The hi and
+//    lo columns of a token are then added with one DPP row rotate.
 //  * Each token's column is computed by the same instructions whatever the
 //    other columns hold, so every token's result equals its own matvec bit
 //    for bit, for any batch size and launch shape.
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
         f32x4 part[UPW];
 #pragma unroll
         for (int un = 0; un < UPW; ++un) {
-            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int L = un * 4; L < un * 4 + 4; ++L) {
                 const float scf =
@@ -341,13 +341,10 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const bf16x8 av = decode8_bf16(cw[L][m], scf);
-                    if (m & 1)
-                        acc1 = mfma16x16x32(av, bv[m], acc1);
-                    else
-                        acc0 = mfma16x16x32(av, bv[m], acc0);
+                    acc = mfma16x16x32(av, bv[m], acc);
                 }
             }
-            part[un] = acc0 + acc1;
+            part[un] = acc;
         }
 
         // ---- 5. sum the units in order, then store
@@ -463,7 +460,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_generic(SkinnyArgs a)
     const uint8_t *srow = Ss + (mat * ROWS_WG + tile * 16 + li) * sstride;
     const __bf16 *bb = Bs + b_row<XBF>(li, tm.ntok) * bstride + ls * 32;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 acc = zero4, acc0 = zero4, acc1 = zero4;
+    f32x4 acc = zero4, uacc = zero4;
     const int nsteps = cpad / 128;
     for (int st = 0; st < nsteps; ++st) {
         const int g = st * 4 + ls;
@@ -477,16 +474,11 @@ __global__ __launch_bounds__(NW * 64) void skinny_generic(SkinnyArgs a)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(bb + st * 128 + m * 8);
-            if (m & 1)
-                acc1 = mfma16x16x32(decode8_bf16(cw[m], scf), bv, acc1);
-            else
-                acc0 = mfma16x16x32(decode8_bf16(cw[m], scf), bv, acc0);
+            uacc = mfma16x16x32(decode8_bf16(cw[m], scf), bv, uacc);
         }
         if ((st & 3) == 3 || st + 1 == nsteps) { // end of a 512-column unit
-            const f32x4 part = acc0 + acc1;
-            acc = st < 4 ? part : acc + part;
-            acc0 = zero4;
-            acc1 = zero4;
+            acc = st < 4 ? uacc : acc + uacc;
+            uacc = zero4;
         }
     }
     if (MODE == MODE_GATEUP) {

@@ -93,6 +93,14 @@ def test_wide_scale_range(m, orc):
     check(m, orc, 128, 1024, 4, 11, lo=60, hi=190)
 
 
+@pytest.mark.parametrize("b,xdt", [(9, "f32"), (23, "f32"), (40, "f32"), (17, "bf16"),
+                                   (40, "bf16"), (64, "bf16")])
+def test_tiled_shapes(m, orc, b, xdt):
+    """Enough row blocks for the tiled kernel (12300 rows, a ragged last
+    block), 1 to 4 column tiles in use, fp32 and bf16 activations."""
+    check(m, orc, 12300, 1024, b, 700 + b, xdt=xdt)
+
+
 def test_many_row_blocks_per_workgroup(m, orc):
     """Tall, narrow weights with 40 tokens: enough workgroups that each one
     walks several row blocks (ragged last block)."""
@@ -115,7 +123,7 @@ def test_batch_equals_matvec_bitwise(m, rows, cols):
             assert np.array_equal(y1.view(np.uint32), yb[t].view(np.uint32)), (b, t)
 
 
-@pytest.mark.parametrize("rows,cols", [(256, 4096), (96, 2048)])
+@pytest.mark.parametrize("rows,cols", [(256, 4096), (96, 2048), (12300, 1024)])
 def test_bf16_batch_equals_single_bitwise(m, rows, cols):
     w, x = inputs.gemm_case(rows + 7, rows, cols, 70, x_dtype="bf16")
     wd = dev(w)
