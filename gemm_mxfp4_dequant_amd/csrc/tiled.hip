@@ -7,21 +7,24 @@
 // canonical summation order), so every token's result is bit-identical to
 // its own matvec.  What differs is the schedule:
 //
-//  * A workgroup of NW waves owns NW * RT * 16 output rows and up to 16 * NC
-//    MFMA columns (16 * NC bf16 tokens, or 8 * NC fp32 tokens as hi/lo
-//    pairs).  Each wave owns RT row tiles of every matrix of the mode (gate
-//    and up tiles of the same rows sit in one wave, so SwiGLU needs no
-//    exchange) and runs the whole K loop.
-//  * K is streamed in 128-column steps.  The activations of a step pass
-//    through registers into a double-buffered LDS slab, shared by all
-//    waves; every decoded weight serves NC column tiles and every
-//    activation fragment read from LDS serves RT * NMAT row tiles.
-//  * The code words, scale bytes and activations of step s + 4 are loaded
-//    together during step s.
-//    Loads of one distance complete in issue order, so waiting for step
-//    s + 1's activations never drains the weight loads behind them.  All
-//    loads are unconditional (indices clamped), which keeps the wait counts
-//    static.
+//  * A workgroup of NW waves owns NW * 16 output rows of every matrix of
+//    the mode (gate and up rows of one wave are the same rows, so SwiGLU
+//    needs no exchange) and up to 16 * NC MFMA columns (16 * NC bf16
+//    tokens, or 8 * NC fp32 tokens as hi/lo pairs), and runs the whole K
+//    loop in 128-column steps.
+//  * Operands stream through a ring of four LDS stages filled by direct
+//    global -> LDS loads (global_load_lds_dwordx4 / _dword): per step, each
+//    wave loads its own 16 rows' code bytes (1 KB per matrix) and scale
+//    bytes, and a share of the step's activation slab (only the tokens the
+//    item has column tiles for), which all waves read.  Three steps are in
+//    flight while one is computed, with no registers held for them.
+//  * Every wave issues the same number of loads per stage, and the loop has
+//    no other vector memory operations, so "stage s has landed" is one
+//    constant vmcnt wait, followed by one workgroup barrier per step (which
+//    also frees the stage loaded next).
+//  * The activation slab is stored XOR-swizzled (16-byte chunk k of token t
+//    at position k ^ (t & 15)), so the 16 lanes reading one MFMA fragment
+//    hit distinct banks.
 //  * Work items come from the same grouping as the skinny kernel
 //    ("rlx-cpu 0.2.17, src/gguf_matmul.rs", grouped_moe_sort_plan): an
 //    expert's rows are streamed once per item of up to 16 * NC tokens
@@ -36,10 +39,8 @@ namespace mx {
 
 namespace {
 
-constexpr int TKS = 128;        // columns per K step
-constexpr int TP = 4;           // steps loaded ahead (= steps per 512-column unit)
-constexpr int TBROW = TKS + 8;  // LDS operand row stride (bf16): lanes of a row tile
-                                // start 272 bytes apart -> distinct banks
+constexpr int TKS = 128; // columns per K step
+constexpr int TNS = 4;   // LDS stages (= steps per 512-column unit)
 
 template <int N> struct IntTag {
     static constexpr int value = N;
@@ -53,22 +54,65 @@ __device__ __forceinline__ int64_t t_token_row(const SkinnyArgs &a, int slot0, i
     return slot0 + t;
 }
 
+// s_waitcnt with vmcnt(n) and the other counters left alone (gfx9 layout).
+template <int N> __device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Direct global -> LDS loads: `bytes` (16 or 4) per lane, lane l's bytes to
+// lds + l * bytes (lds is wave-uniform).  Kept in plain device functions: the
+// kernel templates' host pass must not see the builtin.
+__device__ __forceinline__ void lds_dma16(const void *g, void *lds)
+{
+    __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void *g, void *lds)
+{
+    __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for every
+// load in flight); the compiler barriers keep LDS accesses on their side.
+__device__ __forceinline__ void raw_barrier()
+{
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+}
+
 } // namespace
 
-template <int NW, int RT, int NC, bool XBF, int MODE>
+template <int NW, int NC, bool XBF, int MODE>
 __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
 {
-    constexpr int NT = NW * 64;
     constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
-    constexpr int MT = NMAT * RT;               // A tiles per wave
-    constexpr int RB = NW * RT * 16;            // output rows per workgroup
+    constexpr int ES = XBF ? 2 : 4;             // activation element bytes
     constexpr int NCOL = 16 * NC;               // MFMA columns
     constexpr int TPD = XBF ? NCOL : NCOL / 2;  // tokens per work item
-    constexpr int UNITS = TPD * (TKS / 8);      // 8-element pieces per step
-    constexpr int UPT = UNITS / NT;             // pieces per thread per step
-    static_assert(UNITS % NT == 0, "activation pieces must divide evenly");
+    constexpr int RB = NW * 16;                 // output rows per workgroup
+    constexpr int ROWB = TKS * ES;              // bytes of one token per step
+    constexpr int ACT_BYTES = TPD * ROWB;       // activation slab per step (at most)
+    // stage layout: codes [NW][NMAT][1 KB] | scales [NW][256 B] | slab
+    constexpr int SC_OFF = NW * NMAT * 1024;
+    constexpr int ACT_OFF = SC_OFF + NW * 256;
+    constexpr int STAGE = ACT_OFF + ACT_BYTES;
 
-    __shared__ __align__(16) __bf16 Bs[2][NCOL][TBROW];
+    // one variable per stage: loads into one stage and reads of another are
+    // then known not to alias, and the compiler adds no waits of its own
+    __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+    auto stage = [&] __device__(auto tag) -> uint8_t * {
+        constexpr int k = decltype(tag)::value;
+        if constexpr (k == 0)
+            return st0;
+        else if constexpr (k == 1)
+            return st1;
+        else if constexpr (k == 2)
+            return st2;
+        else
+            return st3;
+    };
 
     const int C = a.cols;
     const int R = a.rows;
@@ -97,101 +141,27 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, ls = lane >> 4;
     const int64_t code_bytes = (int64_t)R * (C / 2);
-
-    // A rows of this lane: tile mt = mat * RT + rt; rows past the end read
-    // row R-1 (never stored; MFMA output rows depend on their own A row only).
-    // Offsets are 32-bit from the tensor base (a tensor is < 2^31 bytes).
     const uint8_t *Am[NMAT];
-    uint32_t aoff[MT], soff[MT];
 #pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat) {
+    for (int mat = 0; mat < NMAT; ++mat)
         Am[mat] = (mat ? a.w1 : a.w0) + (int64_t)expert * a.expert_stride;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int r = min(row0 + (wave * RT + rt) * 16 + li, R - 1);
-            aoff[mat * RT + rt] = (uint32_t)r * (uint32_t)(C / 2) + ls * 16;
-            soff[mat * RT + rt] = (uint32_t)code_bytes + (uint32_t)r * (uint32_t)gpr;
-        }
-    }
 
-    // Activation pieces of this thread: piece q is token t = u / 16, columns
-    // 8 * (u % 16) .. +8 of each step.  Tokens past the item's end re-read its
-    // last token (their columns are never stored; MFMA columns do not mix).
-    int64_t xoff[UPT];
+    // ---- per-lane load sources (rows past the end read row R-1: never
+    // stored, and MFMA output rows depend on their own A row only)
+    const int lrow = min(row0 + wave * 16 + li, R - 1);
+    // codes: lane (li, ls) loads group ls of step s of row li
+    const uint8_t *csrc[NMAT];
 #pragma unroll
-    for (int q = 0; q < UPT; ++q) {
-        const int u = tid + q * NT;
-        const int t = u / (TKS / 8);
-        xoff[q] = t_token_row<MODE>(a, slot0, min(t, ntok - 1)) * C + (u % (TKS / 8)) * 8;
-    }
-
-    u32x4 xr[TP][UPT][XBF ? 1 : 2]; // activation ring (bf16 words / raw fp32)
-    u32x4 cw[TP][MT];               // code ring
-    uint32_t sw[TP][MT];            // scale ring: the 4 scale bytes of a step
-
-    auto load_act = [&](int slot, int s) {
-#pragma unroll
-        for (int q = 0; q < UPT; ++q) {
-            if constexpr (XBF) {
-                xr[slot][q][0] = *reinterpret_cast<const u32x4 *>(
-                    reinterpret_cast<const uint16_t *>(a.x) + xoff[q] + s * TKS);
-            } else {
-                const float *p = reinterpret_cast<const float *>(a.x) + xoff[q] + s * TKS;
-                xr[slot][q][0] = *reinterpret_cast<const u32x4 *>(p);
-                xr[slot][q][1] = *reinterpret_cast<const u32x4 *>(p + 4);
-            }
-        }
-    };
-    auto load_codes = [&](int slot, int s) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const uint8_t *A = Am[mt / RT];
-            cw[slot][mt] = *reinterpret_cast<const u32x4 *>(A + aoff[mt] + s * (TKS / 2));
-            sw[slot][mt] = *reinterpret_cast<const uint32_t *>(A + soff[mt] + s * 4);
-        }
-    };
-    auto store_act = [&](int buf, int slot) {
-#pragma unroll
-        for (int q = 0; q < UPT; ++q) {
-            const int u = tid + q * NT;
-            const int t = u / (TKS / 8), seg = u % (TKS / 8);
-            if constexpr (XBF) {
-                *reinterpret_cast<u32x4 *>(&Bs[buf][t][seg * 8]) = xr[slot][q][0];
-            } else {
-                float v[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[i] = __uint_as_float(xr[slot][q][0][i]);
-                    v[4 + i] = __uint_as_float(xr[slot][q][1][i]);
-                }
-                bf16x8 hi, lo;
-                split_bf16x8(v, hi, lo);
-                const int rowhi = (t / 8) * 16 + (t % 8);
-                *reinterpret_cast<bf16x8 *>(&Bs[buf][rowhi][seg * 8]) = hi;
-                *reinterpret_cast<bf16x8 *>(&Bs[buf][rowhi + 8][seg * 8]) = lo;
-            }
-        }
-    };
-
-    // ---- prologue: steps 0..3, slab 0 -> LDS.  All four steps are waited
-    // for here (step 0 needs its loads anyway), so the loop is entered with
-    // no loads in flight and the compiler counts the loop's own loads
-    // exactly; otherwise the prologue's load order, merged at the loop head,
-    // makes it wait for every load at the top of each 512-column unit.
-#pragma unroll
-    for (int p = 0; p < TP; ++p) {
-        load_act(p, p);
-        load_codes(p, p);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0)
-    store_act(0, 0);
-    __syncthreads();
-
+    for (int mat = 0; mat < NMAT; ++mat)
+        csrc[mat] = Am[mat] + (int64_t)lrow * (C / 2) + ls * 16;
+    // scales: lanes 0-15 the first matrix's rows, 16-31 the second's (or the
+    // first's again); lanes 32-63 repeat lanes 0-31
+    const uint8_t *ssrc = Am[NMAT == 2 ? (ls & 1) : 0] + code_bytes + (int64_t)lrow * gpr;
     // acc: the current 512-column unit, its 16 MFMA steps in k order; tot:
     // the units so far, summed in ascending order
-    f32x4 acc[MT][NC], tot[MT][NC];
+    f32x4 acc[NMAT][NC], tot[NMAT][NC];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             acc[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -199,48 +169,119 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
         }
 
     // The K loop, specialised on the column tiles in use (NCU <= NC) so that
-    // its body has no branches.
-    auto k_loop = [&](auto ncu_tag) {
+    // its body has no branches and the slab loads cover only the tokens it
+    // reads: 16 bf16 / 8 fp32 tokens for one tile (4-byte loads), 32 / 16 for
+    // two, the whole item for more (16-byte loads).  Every wave issues the
+    // same number of loads per step either way.
+    auto k_loop = [&] __device__(auto ncu_tag) {
         constexpr int NCU = decltype(ncu_tag)::value;
+        constexpr int TT = XBF ? 16 : 8; // tokens per column tile
+        constexpr int TN = NCU == 1 ? TT : (NCU == 2 ? 2 * TT : TPD);
+        constexpr int SB = TN * ROWB;                 // slab bytes loaded per step
+        constexpr bool DW = NCU == 1;                 // 4-byte loads
+        constexpr int PIECE = DW ? 256 : 1024;        // bytes per wave load
+        constexpr int AIN = SB / (NW * PIECE);        // slab loads per wave per step
+        static_assert(SB % (NW * PIECE) == 0 && AIN >= 1, "slab loads must divide evenly");
+        constexpr int GN = NMAT + 1 + AIN;            // loads per wave per step
+
+        // slab: load i of this wave fills bytes [(wave * AIN + i) * PIECE,
+        // +PIECE) of the slab; the bytes at slab offset o belong to token
+        // t = o / ROWB, 16-byte position p, i.e. chunk k = p ^ (t & 15)
+        const uint8_t *xsrc[AIN];
+#pragma unroll
+        for (int i = 0; i < AIN; ++i) {
+            const int o = (wave * AIN + i) * PIECE + lane * (DW ? 4 : 16);
+            const int t = o / ROWB, p = (o % ROWB) / 16;
+            const int k = p ^ (t & 15);
+            const int64_t row = t_token_row<MODE>(a, slot0, min(t, ntok - 1));
+            xsrc[i] = reinterpret_cast<const uint8_t *>(a.x) + (row * C) * ES + k * 16 + o % 16;
+        }
+        auto issue = [&] __device__(auto tag, int s) {
+            uint8_t *S = stage(tag);
+#pragma unroll
+            for (int mat = 0; mat < NMAT; ++mat)
+                lds_dma16(csrc[mat] + s * (TKS / 2), S + (wave * NMAT + mat) * 1024);
+            lds_dma4(ssrc + s * 4, S + SC_OFF + wave * 256);
+#pragma unroll
+            for (int i = 0; i < AIN; ++i) {
+                if constexpr (DW)
+                    lds_dma4(xsrc[i] + s * ROWB, S + ACT_OFF + (wave * AIN + i) * PIECE);
+                else
+                    lds_dma16(xsrc[i] + s * ROWB, S + ACT_OFF + (wave * AIN + i) * PIECE);
+            }
+        };
+
+        // prologue: the token gathers above have landed; steps 0..2 in flight
+        wait_vmcnt<0>();
+        issue(IntTag<0>{}, 0);
+        issue(IntTag<1>{}, min(1, nsteps - 1));
+        issue(IntTag<2>{}, min(2, nsteps - 1));
+
         for (int un = 0; un < nunits; ++un) {
+            auto step = [&] __device__(auto jt) {
+                constexpr int j = decltype(jt)::value;
+                const int s = un * TNS + j;
+                // stage j (step s) has landed for every wave; stage j - 1
+                // (step s - 1) is free
+                wait_vmcnt<(TNS - 2) * GN>();
+                raw_barrier();
+                issue(IntTag<(j + 3) % TNS>{}, min(s + 3, nsteps - 1));
+
+                const uint8_t *S = stage(IntTag<j>{});
+                u32x4 cw[NMAT];
+                float scf[NMAT];
 #pragma unroll
-            for (int j = 0; j < TP; ++j) {
-                const int s = un * TP + j;
-                // Keep each step's instructions inside its step: hoisting a
-                // later step's scale extraction to the top of the loop would
-                // wait for loads issued at the end of the previous iteration.
-                __builtin_amdgcn_sched_barrier(0);
-                // ---- step s: decode + MFMA from slab j & 1 and code slot j
-                float scf[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    scf[mt] = e8m0_operand_of(sw[j][mt], ls);
+                for (int mt = 0; mt < NMAT; ++mt) {
+                    cw[mt] = *reinterpret_cast<const u32x4 *>(S + (wave * NMAT + mt) * 1024 +
+                                                              (ls * 16 + li) * 16);
+                    scf[mt] = e8m0_operand_of(*reinterpret_cast<const uint32_t *>(
+                                                  S + SC_OFF + wave * 256 + (mt * 16 + li) * 4),
+                                              ls);
+                }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     bf16x8 bv[NCU];
 #pragma unroll
-                    for (int c = 0; c < NCU; ++c)
-                        bv[c] = *reinterpret_cast<const bf16x8 *>(
-                            &Bs[j & 1][c * 16 + li][ls * 32 + m * 8]);
+                    for (int c = 0; c < NCU; ++c) {
+                        if constexpr (XBF) {
+                            const int t = c * 16 + li;
+                            const int p = (4 * ls + m) ^ li;
+                            bv[c] = *reinterpret_cast<const bf16x8 *>(S + ACT_OFF + t * ROWB +
+                                                                      p * 16);
+                        } else {
+                            const int t = c * 8 + (li & 7);
+                            const int k0 = 8 * ls + 2 * m;
+                            const f32x4 v0 = *reinterpret_cast<const f32x4 *>(
+                                S + ACT_OFF + t * ROWB + (k0 ^ (t & 15)) * 16);
+                            const f32x4 v1 = *reinterpret_cast<const f32x4 *>(
+                                S + ACT_OFF + t * ROWB + ((k0 + 1) ^ (t & 15)) * 16);
+                            float v[8];
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const bf16x8 av = decode8_bf16(cw[j][mt][m], scf[mt]);
+                            for (int i = 0; i < 4; ++i) {
+                                v[i] = v0[i];
+                                v[4 + i] = v1[i];
+                            }
+                            bf16x8 hi, lo;
+                            split_bf16x8(v, hi, lo);
+                            bv[c] = li < 8 ? hi : lo;
+                        }
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < NMAT; ++mt) {
+                        const bf16x8 av = decode8_bf16(cw[mt][m], scf[mt]);
 #pragma unroll
                         for (int c = 0; c < NCU; ++c)
                             acc[mt][c] = mfma16x16x32(av, bv[c], acc[mt][c]);
                     }
                 }
-                // ---- loads of step s + 4 (the last step re-loaded past the end)
-                const int sl = min(s + TP, nsteps - 1);
-                load_act(j, sl);
-                load_codes(j, sl);
-                // ---- step s + 1's activations -> the other slab
-                store_act((j + 1) & 1, (j + 1) % TP);
-                __syncthreads();
-            }
+            };
+            step(IntTag<0>{});
+            step(IntTag<1>{});
+            step(IntTag<2>{});
+            step(IntTag<3>{});
             // ---- end of a 512-column unit
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
                 for (int c = 0; c < NCU; ++c) {
                     tot[mt][c] = un == 0 ? acc[mt][c] : tot[mt][c] + acc[mt][c];
@@ -256,45 +297,44 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
         k_loop(IntTag<2>{});
     else
         k_loop(IntTag<1>{});
+    // the last steps' (clamped, unused) loads land before the workgroup ends
+    wait_vmcnt<0>();
 
     // ---- outputs
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            if (c >= nct)
-                continue;
-            f32x4 g = tot[rt][c];
-            f32x4 u = g;
-            if (MODE == MODE_GATEUP)
-                u = tot[RT + rt][c];
-            if (!XBF) { // hi column li + lo column li + 8
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    g[i] += dpp_row_ror8(g[i]);
-                    if (MODE == MODE_GATEUP)
-                        u[i] += dpp_row_ror8(u[i]);
-                }
-            }
-            const int tok = XBF ? c * 16 + li : c * 8 + li;
-            const bool ok = XBF ? tok < ntok : (li < 8 && tok < ntok);
-            if (!ok)
-                continue;
-            const int rbase = row0 + (wave * RT + rt) * 16 + 4 * ls;
-            const int64_t orow = slot0 + tok;
+    for (int c = 0; c < NC; ++c) {
+        if (c >= nct)
+            continue;
+        f32x4 g = tot[0][c];
+        f32x4 u = g;
+        if (MODE == MODE_GATEUP)
+            u = tot[NMAT - 1][c];
+        if (!XBF) { // hi column li + lo column li + 8
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = rbase + i;
-                if (r >= R)
-                    continue;
-                float v = g[i];
+                g[i] += dpp_row_ror8(g[i]);
                 if (MODE == MODE_GATEUP)
-                    v = silu(g[i]) * u[i];
-                if (MODE != MODE_DOWN && a.y_bf16)
-                    reinterpret_cast<uint16_t *>(a.y)[orow * R + r] = f32_to_bf16_bits(v);
-                else
-                    reinterpret_cast<float *>(a.y)[orow * R + r] = v;
+                    u[i] += dpp_row_ror8(u[i]);
             }
+        }
+        const int tok = XBF ? c * 16 + li : c * 8 + li;
+        const bool ok = XBF ? tok < ntok : (li < 8 && tok < ntok);
+        if (!ok)
+            continue;
+        const int rbase = row0 + wave * 16 + 4 * ls;
+        const int64_t orow = slot0 + tok;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rbase + i;
+            if (r >= R)
+                continue;
+            float v = g[i];
+            if (MODE == MODE_GATEUP)
+                v = silu(g[i]) * u[i];
+            if (MODE != MODE_DOWN && a.y_bf16)
+                reinterpret_cast<uint16_t *>(a.y)[orow * R + r] = f32_to_bf16_bits(v);
+            else
+                reinterpret_cast<float *>(a.y)[orow * R + r] = v;
         }
     }
 }
@@ -312,10 +352,10 @@ struct TEntry {
     TiledFn fn;
 };
 
-#define MX_T(MODE, XBF, NW, NC) {MODE, XBF, NW, NC, tiled_kernel<NW, 1, NC, (bool)XBF, MODE>}
+#define MX_T(MODE, XBF, NW, NC) {MODE, XBF, NW, NC, tiled_kernel<NW, NC, (bool)XBF, MODE>}
 #define MX_TM(MODE) \
     MX_T(MODE, 0, 8, 4), MX_T(MODE, 1, 8, 4), MX_T(MODE, 0, 4, 4), MX_T(MODE, 1, 4, 4), \
-        MX_T(MODE, 0, 4, 2), MX_T(MODE, 1, 4, 2), MX_T(MODE, 1, 8, 2)
+        MX_T(MODE, 0, 4, 2), MX_T(MODE, 1, 4, 2), MX_T(MODE, 0, 8, 2), MX_T(MODE, 1, 8, 2)
 
 const TEntry kTiled[] = {MX_TM(MODE_GEMM), MX_TM(MODE_GATEUP), MX_TM(MODE_DOWN)};
 

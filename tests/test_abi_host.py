@@ -42,6 +42,21 @@ def test_exports_every_declared_symbol(m):
         assert hasattr(L, n), n
 
 
+def test_no_undefined_library_symbols():
+    """Every kernel the library launches is defined in it: a kernel template
+    whose host stub the compiler dropped shows up here as an undefined mx::
+    symbol, long before a GPU run would fail to load the library."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "-C", "--undefined-only", LIB], capture_output=True,
+                         text=True, check=True).stdout
+    bad = [l for l in out.splitlines() if "mx::" in l]
+    assert not bad, bad
+
+
 def test_nbytes(m):
     assert m.mxfp4_nbytes(2304, 5120) == 2304 * 5120 * 17 // 32
     assert m.mxfp4_nbytes(1, 32) == 17
