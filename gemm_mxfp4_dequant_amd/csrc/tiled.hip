@@ -94,14 +94,16 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     constexpr int RB = NW * 16;                 // output rows per workgroup
     constexpr int ROWB = TKS * ES;              // bytes of one token per step
     constexpr int ACT_BYTES = TPD * ROWB;       // activation slab per step (at most)
-    // stage layout: codes [NW][NMAT][1 KB] | scales [NW][256 B] | slab
-    constexpr int SC_OFF = NW * NMAT * 1024;
-    constexpr int ACT_OFF = SC_OFF + NW * 256;
+    // stage layout: codes [NW][NMAT][1 KB] | slab
+    constexpr int ACT_OFF = NW * NMAT * 1024;
     constexpr int STAGE = ACT_OFF + ACT_BYTES;
 
     // one variable per stage: loads into one stage and reads of another are
     // then known not to alias, and the compiler adds no waits of its own
     __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+    // scale bytes of one 512-column unit: [NW][64 lanes][16 B], loaded with
+    // stage 0 (the unit's first step) and read into registers at that step
+    __shared__ __align__(16) uint8_t scs[NW * 1024];
     auto stage = [&] __device__(auto tag) -> uint8_t * {
         constexpr int k = decltype(tag)::value;
         if constexpr (k == 0)
@@ -154,8 +156,8 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat)
         csrc[mat] = Am[mat] + (int64_t)lrow * (C / 2) + ls * 16;
-    // scales: lanes 0-15 the first matrix's rows, 16-31 the second's (or the
-    // first's again); lanes 32-63 repeat lanes 0-31
+    // scales: lane (li, ls) loads the 16 scale bytes of a unit for row li of
+    // matrix ls % NMAT (lanes of a repeated matrix load the same bytes)
     const uint8_t *ssrc = Am[NMAT == 2 ? (ls & 1) : 0] + code_bytes + (int64_t)lrow * gpr;
     // acc: the current 512-column unit, its 16 MFMA steps in k order; tot:
     // the units so far, summed in ascending order
@@ -176,39 +178,37 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     auto k_loop = [&] __device__(auto ncu_tag) {
         constexpr int NCU = decltype(ncu_tag)::value;
         constexpr int TT = XBF ? 16 : 8; // tokens per column tile
-        constexpr int TN = NCU == 1 ? TT : (NCU == 2 ? 2 * TT : TPD);
+        constexpr int TMIN = NW * 1024 / ROWB;        // one 16-byte load per wave
+        constexpr int TN0 = NCU <= 2 ? NCU * TT : TPD;
+        constexpr int TN = TN0 < TMIN ? TMIN : TN0;   // tokens loaded per step
         constexpr int SB = TN * ROWB;                 // slab bytes loaded per step
-        constexpr bool DW = NCU == 1;                 // 4-byte loads
-        constexpr int PIECE = DW ? 256 : 1024;        // bytes per wave load
-        constexpr int AIN = SB / (NW * PIECE);        // slab loads per wave per step
-        static_assert(SB % (NW * PIECE) == 0 && AIN >= 1, "slab loads must divide evenly");
-        constexpr int GN = NMAT + 1 + AIN;            // loads per wave per step
+        constexpr int AIN = SB / (NW * 1024);         // slab loads per wave per step
+        static_assert(SB % (NW * 1024) == 0 && AIN >= 1 && TN <= TPD, "slab loads");
+        constexpr int GN = NMAT + AIN;                // loads per wave per step (+1 scale
+                                                      // load with stage 0)
 
-        // slab: load i of this wave fills bytes [(wave * AIN + i) * PIECE,
-        // +PIECE) of the slab; the bytes at slab offset o belong to token
+        // slab: load i of this wave fills bytes [(wave * AIN + i) KB, +1 KB)
+        // of the slab; the 16 bytes at slab offset o belong to token
         // t = o / ROWB, 16-byte position p, i.e. chunk k = p ^ (t & 15)
         const uint8_t *xsrc[AIN];
 #pragma unroll
         for (int i = 0; i < AIN; ++i) {
-            const int o = (wave * AIN + i) * PIECE + lane * (DW ? 4 : 16);
+            const int o = (wave * AIN + i) * 1024 + lane * 16;
             const int t = o / ROWB, p = (o % ROWB) / 16;
             const int k = p ^ (t & 15);
             const int64_t row = t_token_row<MODE>(a, slot0, min(t, ntok - 1));
-            xsrc[i] = reinterpret_cast<const uint8_t *>(a.x) + (row * C) * ES + k * 16 + o % 16;
+            xsrc[i] = reinterpret_cast<const uint8_t *>(a.x) + (row * C) * ES + k * 16;
         }
         auto issue = [&] __device__(auto tag, int s) {
             uint8_t *S = stage(tag);
 #pragma unroll
             for (int mat = 0; mat < NMAT; ++mat)
                 lds_dma16(csrc[mat] + s * (TKS / 2), S + (wave * NMAT + mat) * 1024);
-            lds_dma4(ssrc + s * 4, S + SC_OFF + wave * 256);
 #pragma unroll
-            for (int i = 0; i < AIN; ++i) {
-                if constexpr (DW)
-                    lds_dma4(xsrc[i] + s * ROWB, S + ACT_OFF + (wave * AIN + i) * PIECE);
-                else
-                    lds_dma16(xsrc[i] + s * ROWB, S + ACT_OFF + (wave * AIN + i) * PIECE);
-            }
+            for (int i = 0; i < AIN; ++i)
+                lds_dma16(xsrc[i] + s * ROWB, S + ACT_OFF + (wave * AIN + i) * 1024);
+            if constexpr (decltype(tag)::value == 0) // a unit's first step: its scales
+                lds_dma16(ssrc + (s / 4) * 16, scs + wave * 1024);
         };
 
         // prologue: the token gathers above have landed; steps 0..2 in flight
@@ -217,26 +217,33 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
         issue(IntTag<1>{}, min(1, nsteps - 1));
         issue(IntTag<2>{}, min(2, nsteps - 1));
 
+        u32x4 usc[NMAT]; // scale bytes of the current unit: word j = step j
         for (int un = 0; un < nunits; ++un) {
             auto step = [&] __device__(auto jt) {
                 constexpr int j = decltype(jt)::value;
                 const int s = un * TNS + j;
                 // stage j (step s) has landed for every wave; stage j - 1
-                // (step s - 1) is free
-                wait_vmcnt<(TNS - 2) * GN>();
+                // (step s - 1) is free.  Loads issued after stage j's: two
+                // steps' worth, plus the scale load of the stage-0 step when
+                // that is one of them (j = 2, 3).
+                wait_vmcnt<(TNS - 2) * GN + (j >= 2 ? 1 : 0)>();
                 raw_barrier();
                 issue(IntTag<(j + 3) % TNS>{}, min(s + 3, nsteps - 1));
 
                 const uint8_t *S = stage(IntTag<j>{});
+                if constexpr (j == 0) { // this unit's scales, before they are refilled
+#pragma unroll
+                    for (int mt = 0; mt < NMAT; ++mt)
+                        usc[mt] = *reinterpret_cast<const u32x4 *>(scs + wave * 1024 +
+                                                                   (mt * 16 + li) * 16);
+                }
                 u32x4 cw[NMAT];
                 float scf[NMAT];
 #pragma unroll
                 for (int mt = 0; mt < NMAT; ++mt) {
                     cw[mt] = *reinterpret_cast<const u32x4 *>(S + (wave * NMAT + mt) * 1024 +
                                                               (ls * 16 + li) * 16);
-                    scf[mt] = e8m0_operand_of(*reinterpret_cast<const uint32_t *>(
-                                                  S + SC_OFF + wave * 256 + (mt * 16 + li) * 4),
-                                              ls);
+                    scf[mt] = e8m0_operand_of(usc[mt][j], ls);
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
