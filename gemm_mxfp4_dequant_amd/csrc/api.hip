@@ -86,6 +86,8 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 // Tiled path: waves per workgroup (expert bank / GEMM), and the mean pairs
 // per touched expert from which the expert bank uses it.
 constexpr int TILED_NW_MOE = 8;
+constexpr int TILED_RT_GATEUP = 1; // four 32 KB LDS stages
+constexpr int TILED_RT_DOWN = 2;   // one activation slab serves 256 rows
 constexpr int TILED_NW_GEMM = 4;
 constexpr int TILED_NC = 4;
 constexpr int TILED_MIN_TOKENS = 8;
@@ -237,7 +239,8 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
         a.n_work = n_work;
         a.token_of_slot = tos;
         if (tiled) {
-            TRY(launched(mx::tiled_launch(mx::MODE_GATEUP, xbf, TILED_NW_MOE, TILED_NC, a, st),
+            TRY(launched(mx::tiled_launch(mx::MODE_GATEUP, xbf, TILED_NW_MOE, TILED_RT_GATEUP,
+                                          TILED_NC, a, st),
                          "gate/up"));
         } else {
             const mx::SkinnyShape sh =
@@ -263,7 +266,8 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
         a.work = work;
         a.n_work = n_work;
         if (tiled) {
-            TRY(launched(mx::tiled_launch(mx::MODE_DOWN, xbf, TILED_NW_MOE, TILED_NC, a, st),
+            TRY(launched(mx::tiled_launch(mx::MODE_DOWN, xbf, TILED_NW_MOE, TILED_RT_DOWN,
+                                          TILED_NC, a, st),
                          "down"));
         } else {
             const mx::SkinnyShape sh =
@@ -316,7 +320,7 @@ int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_d
     const int maxc = xbf ? 16 : 8;
     const int tnc = b <= mx::tiled_tokens(xbf, 2) ? 2 : TILED_NC;
     const int64_t tnch = (b + mx::tiled_tokens(xbf, tnc) - 1) / mx::tiled_tokens(xbf, tnc);
-    const int rpw = mx::tiled_rows_per_wg(TILED_NW_GEMM);
+    const int rpw = mx::tiled_rows_per_wg(TILED_NW_GEMM, 1);
     const int64_t twgs = tnch * ((rows + rpw - 1) / rpw);
     if (xbf && b > maxc && mx::tiled_supported((int)cols) && twgs >= TILED_MIN_WGS) {
         // bf16 tokens beyond one skinny chunk and enough row blocks to fill
@@ -339,7 +343,7 @@ int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_d
         a.y = y;
         a.y_bf16 = y_dtype == MXFP4_BF16;
         return launched(
-            mx::tiled_launch(mx::MODE_GEMM, xbf, TILED_NW_GEMM, nc, a, (hipStream_t)stream),
+            mx::tiled_launch(mx::MODE_GEMM, xbf, TILED_NW_GEMM, 1, nc, a, (hipStream_t)stream),
             "gemm");
     }
     const int tpc = mx::skinny_pick_tpc(mx::MODE_GEMM, xbf, (int)cols, b < maxc ? (int)b : maxc);

@@ -44,13 +44,13 @@ int64_t skinny_blocks(const SkinnyShape &s, int rows, int nch);
 hipError_t skinny_launch(int mode, bool xbf, const SkinnyShape &s, SkinnyArgs a,
                          hipStream_t stream);
 
-// Tiled path (items of tens of tokens): NW waves x 16 rows per workgroup,
+// Tiled path (items of tens of tokens): NW waves x RT x 16 rows per workgroup,
 // NC column tiles of 16 MFMA columns, K streamed in 128-column steps.
 bool tiled_supported(int cols);     // cols % 512 == 0
 int tiled_tokens(bool xbf, int nc); // tokens per work item
-int tiled_rows_per_wg(int nw);
-// grid = ceil(rows / tiled_rows_per_wg(nw)) * a.nch
-hipError_t tiled_launch(int mode, bool xbf, int nw, int nc, const SkinnyArgs &a,
+int tiled_rows_per_wg(int nw, int rt);
+// grid = ceil(rows / tiled_rows_per_wg(nw, rt)) * a.nch
+hipError_t tiled_launch(int mode, bool xbf, int nw, int rt, int nc, const SkinnyArgs &a,
                         hipStream_t stream);
 
 hipError_t dequant_launch(const uint8_t *w, int64_t rows, int64_t cols, void *out, bool bf16,

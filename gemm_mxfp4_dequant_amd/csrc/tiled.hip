@@ -7,9 +7,9 @@
 // canonical summation order), so every token's result is bit-identical to
 // its own matvec.  What differs is the schedule:
 //
-//  * A workgroup of NW waves owns NW * 16 output rows of every matrix of
-//    the mode (gate and up rows of one wave are the same rows, so SwiGLU
-//    needs no exchange) and up to 16 * NC MFMA columns (16 * NC bf16
+//  * A workgroup of NW waves owns NW * RT * 16 output rows of every matrix
+//    of the mode, RT row tiles per wave (gate and up rows of one wave are the
+//    same rows, so SwiGLU needs no exchange) and up to 16 * NC MFMA columns (16 * NC bf16
 //    tokens, or 8 * NC fp32 tokens as hi/lo pairs), and runs the whole K
 //    loop in 128-column steps.
 //  * Operands stream through a ring of four LDS stages filled by direct
@@ -84,18 +84,20 @@ __device__ __forceinline__ void raw_barrier()
 
 } // namespace
 
-template <int NW, int NC, bool XBF, int MODE>
+template <int NW, int RT, int NC, bool XBF, int MODE>
 __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
 {
     constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
+    constexpr int MT = NMAT * RT;               // A tiles per wave: tile mt = mat * RT + rt
+    static_assert(MT <= 4, "one 16-byte scale load per wave covers at most 4 tiles");
     constexpr int ES = XBF ? 2 : 4;             // activation element bytes
     constexpr int NCOL = 16 * NC;               // MFMA columns
     constexpr int TPD = XBF ? NCOL : NCOL / 2;  // tokens per work item
-    constexpr int RB = NW * 16;                 // output rows per workgroup
+    constexpr int RB = NW * RT * 16;            // output rows per workgroup
     constexpr int ROWB = TKS * ES;              // bytes of one token per step
     constexpr int ACT_BYTES = TPD * ROWB;       // activation slab per step (at most)
-    // stage layout: codes [NW][NMAT][1 KB] | slab
-    constexpr int ACT_OFF = NW * NMAT * 1024;
+    // stage layout: codes [NW][MT][1 KB] | slab
+    constexpr int ACT_OFF = NW * MT * 1024;
     constexpr int STAGE = ACT_OFF + ACT_BYTES;
 
     // one variable per stage: loads into one stage and reads of another are
@@ -150,20 +152,21 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
 
     // ---- per-lane load sources (rows past the end read row R-1: never
     // stored, and MFMA output rows depend on their own A row only)
-    const int lrow = min(row0 + wave * 16 + li, R - 1);
-    // codes: lane (li, ls) loads group ls of step s of row li
-    const uint8_t *csrc[NMAT];
+    auto lrow = [&] __device__(int rt) { return min(row0 + (wave * RT + rt) * 16 + li, R - 1); };
+    // codes: lane (li, ls) loads group ls of step s of row li of each tile
+    const uint8_t *csrc[MT];
 #pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat)
-        csrc[mat] = Am[mat] + (int64_t)lrow * (C / 2) + ls * 16;
+    for (int mt = 0; mt < MT; ++mt)
+        csrc[mt] = Am[mt / RT] + (int64_t)lrow(mt % RT) * (C / 2) + ls * 16;
     // scales: lane (li, ls) loads the 16 scale bytes of a unit for row li of
-    // matrix ls % NMAT (lanes of a repeated matrix load the same bytes)
-    const uint8_t *ssrc = Am[NMAT == 2 ? (ls & 1) : 0] + code_bytes + (int64_t)lrow * gpr;
+    // tile ls % MT (lanes of a repeated tile load the same bytes)
+    const int smt = ls % MT;
+    const uint8_t *ssrc = Am[smt / RT] + code_bytes + (int64_t)lrow(smt % RT) * gpr;
     // acc: the current 512-column unit, its 16 MFMA steps in k order; tot:
     // the units so far, summed in ascending order
-    f32x4 acc[NMAT][NC], tot[NMAT][NC];
+    f32x4 acc[MT][NC], tot[MT][NC];
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             acc[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
         constexpr int SB = TN * ROWB;                 // slab bytes loaded per step
         constexpr int AIN = SB / (NW * 1024);         // slab loads per wave per step
         static_assert(SB % (NW * 1024) == 0 && AIN >= 1 && TN <= TPD, "slab loads");
-        constexpr int GN = NMAT + AIN;                // loads per wave per step (+1 scale
+        constexpr int GN = MT + AIN;                  // loads per wave per step (+1 scale
                                                       // load with stage 0)
 
         // slab: load i of this wave fills bytes [(wave * AIN + i) KB, +1 KB)
@@ -202,8 +205,8 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
         auto issue = [&] __device__(auto tag, int s) {
             uint8_t *S = stage(tag);
 #pragma unroll
-            for (int mat = 0; mat < NMAT; ++mat)
-                lds_dma16(csrc[mat] + s * (TKS / 2), S + (wave * NMAT + mat) * 1024);
+            for (int mt = 0; mt < MT; ++mt)
+                lds_dma16(csrc[mt] + s * (TKS / 2), S + (wave * MT + mt) * 1024);
 #pragma unroll
             for (int i = 0; i < AIN; ++i)
                 lds_dma16(xsrc[i] + s * ROWB, S + ACT_OFF + (wave * AIN + i) * 1024);
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
         issue(IntTag<1>{}, min(1, nsteps - 1));
         issue(IntTag<2>{}, min(2, nsteps - 1));
 
-        u32x4 usc[NMAT]; // scale bytes of the current unit: word j = step j
+        u32x4 usc[MT]; // scale bytes of the current unit: word j = step j
         for (int un = 0; un < nunits; ++un) {
             auto step = [&] __device__(auto jt) {
                 constexpr int j = decltype(jt)::value;
@@ -233,15 +236,15 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
                 const uint8_t *S = stage(IntTag<j>{});
                 if constexpr (j == 0) { // this unit's scales, before they are refilled
 #pragma unroll
-                    for (int mt = 0; mt < NMAT; ++mt)
+                    for (int mt = 0; mt < MT; ++mt)
                         usc[mt] = *reinterpret_cast<const u32x4 *>(scs + wave * 1024 +
                                                                    (mt * 16 + li) * 16);
                 }
-                u32x4 cw[NMAT];
-                float scf[NMAT];
+                u32x4 cw[MT];
+                float scf[MT];
 #pragma unroll
-                for (int mt = 0; mt < NMAT; ++mt) {
-                    cw[mt] = *reinterpret_cast<const u32x4 *>(S + (wave * NMAT + mt) * 1024 +
+                for (int mt = 0; mt < MT; ++mt) {
+                    cw[mt] = *reinterpret_cast<const u32x4 *>(S + (wave * MT + mt) * 1024 +
                                                               (ls * 16 + li) * 16);
                     scf[mt] = e8m0_operand_of(usc[mt][j], ls);
                 }
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
                         }
                     }
 #pragma unroll
-                    for (int mt = 0; mt < NMAT; ++mt) {
+                    for (int mt = 0; mt < MT; ++mt) {
                         const bf16x8 av = decode8_bf16(cw[mt][m], scf[mt]);
 #pragma unroll
                         for (int c = 0; c < NCU; ++c)
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
             step(IntTag<3>{});
             // ---- end of a 512-column unit
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int c = 0; c < NCU; ++c) {
                     tot[mt][c] = un == 0 ? acc[mt][c] : tot[mt][c] + acc[mt][c];
@@ -309,39 +312,42 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
 
     // ---- outputs
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        if (c >= nct)
-            continue;
-        f32x4 g = tot[0][c];
-        f32x4 u = g;
-        if (MODE == MODE_GATEUP)
-            u = tot[NMAT - 1][c];
-        if (!XBF) { // hi column li + lo column li + 8
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (c >= nct)
+                continue;
+            f32x4 g = tot[rt][c];
+            f32x4 u = g;
+            if (MODE == MODE_GATEUP)
+                u = tot[RT + rt][c];
+            if (!XBF) { // hi column li + lo column li + 8
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    g[i] += dpp_row_ror8(g[i]);
+                    if (MODE == MODE_GATEUP)
+                        u[i] += dpp_row_ror8(u[i]);
+                }
+            }
+            const int tok = XBF ? c * 16 + li : c * 8 + li;
+            const bool ok = XBF ? tok < ntok : (li < 8 && tok < ntok);
+            if (!ok)
+                continue;
+            const int rbase = row0 + (wave * RT + rt) * 16 + 4 * ls;
+            const int64_t orow = slot0 + tok;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                g[i] += dpp_row_ror8(g[i]);
+                const int r = rbase + i;
+                if (r >= R)
+                    continue;
+                float v = g[i];
                 if (MODE == MODE_GATEUP)
-                    u[i] += dpp_row_ror8(u[i]);
+                    v = silu(g[i]) * u[i];
+                if (MODE != MODE_DOWN && a.y_bf16)
+                    reinterpret_cast<uint16_t *>(a.y)[orow * R + r] = f32_to_bf16_bits(v);
+                else
+                    reinterpret_cast<float *>(a.y)[orow * R + r] = v;
             }
-        }
-        const int tok = XBF ? c * 16 + li : c * 8 + li;
-        const bool ok = XBF ? tok < ntok : (li < 8 && tok < ntok);
-        if (!ok)
-            continue;
-        const int rbase = row0 + wave * 16 + 4 * ls;
-        const int64_t orow = slot0 + tok;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rbase + i;
-            if (r >= R)
-                continue;
-            float v = g[i];
-            if (MODE == MODE_GATEUP)
-                v = silu(g[i]) * u[i];
-            if (MODE != MODE_DOWN && a.y_bf16)
-                reinterpret_cast<uint16_t *>(a.y)[orow * R + r] = f32_to_bf16_bits(v);
-            else
-                reinterpret_cast<float *>(a.y)[orow * R + r] = v;
         }
     }
 }
@@ -355,21 +361,26 @@ namespace {
 typedef void (*TiledFn)(SkinnyArgs);
 
 struct TEntry {
-    int mode, xbf, nw, nc;
+    int mode, xbf, nw, rt, nc;
     TiledFn fn;
 };
 
-#define MX_T(MODE, XBF, NW, NC) {MODE, XBF, NW, NC, tiled_kernel<NW, NC, (bool)XBF, MODE>}
-#define MX_TM(MODE) \
-    MX_T(MODE, 0, 8, 4), MX_T(MODE, 1, 8, 4), MX_T(MODE, 0, 4, 4), MX_T(MODE, 1, 4, 4), \
-        MX_T(MODE, 0, 4, 2), MX_T(MODE, 1, 4, 2), MX_T(MODE, 0, 8, 2), MX_T(MODE, 1, 8, 2)
+#define MX_T(MODE, XBF, NW, RT, NC) \
+    {MODE, XBF, NW, RT, NC, tiled_kernel<NW, RT, NC, (bool)XBF, MODE>}
+#define MX_TX(MODE, NW, RT, NC) MX_T(MODE, 0, NW, RT, NC), MX_T(MODE, 1, NW, RT, NC)
+// expert bank: gate/up 8 waves x 1 row tile (four 32 KB stages), down 8 x 2
+// (one activation slab serves 256 rows: 1.67 -> 1.59 ms on the prefill bank);
+// GEMM: 4 waves x 1 row tile (more workgroups on 14336-row weights)
+// (GEMMs take this path with bf16 tokens only)
+const TEntry kTiled[] = {
+    MX_TX(MODE_GATEUP, 8, 1, 4), MX_TX(MODE_DOWN, 8, 2, 4),
+    MX_T(MODE_GEMM, 1, 4, 1, 4), MX_T(MODE_GEMM, 1, 4, 1, 2),
+};
 
-const TEntry kTiled[] = {MX_TM(MODE_GEMM), MX_TM(MODE_GATEUP), MX_TM(MODE_DOWN)};
-
-const TEntry *tfind(int mode, bool xbf, int nw, int nc)
+const TEntry *tfind(int mode, bool xbf, int nw, int rt, int nc)
 {
     for (const TEntry &e : kTiled)
-        if (e.mode == mode && e.xbf == (int)xbf && e.nw == nw && e.nc == nc)
+        if (e.mode == mode && e.xbf == (int)xbf && e.nw == nw && e.rt == rt && e.nc == nc)
             return &e;
     return nullptr;
 }
@@ -380,15 +391,16 @@ bool tiled_supported(int cols) { return cols % 512 == 0; }
 
 int tiled_tokens(bool xbf, int nc) { return xbf ? 16 * nc : 8 * nc; }
 
-int tiled_rows_per_wg(int nw) { return nw * 16; }
+int tiled_rows_per_wg(int nw, int rt) { return nw * rt * 16; }
 
-hipError_t tiled_launch(int mode, bool xbf, int nw, int nc, const SkinnyArgs &a,
+hipError_t tiled_launch(int mode, bool xbf, int nw, int rt, int nc, const SkinnyArgs &a,
                         hipStream_t stream)
 {
-    const TEntry *e = tfind(mode, xbf, nw, nc);
+    const TEntry *e = tfind(mode, xbf, nw, rt, nc);
     if (!e)
         return hipErrorInvalidValue;
-    const int64_t nrb = (a.rows + tiled_rows_per_wg(nw) - 1) / tiled_rows_per_wg(nw);
+    const int rpw = tiled_rows_per_wg(nw, rt);
+    const int64_t nrb = (a.rows + rpw - 1) / rpw;
     hipLaunchKernelGGL(e->fn, dim3((unsigned)(nrb * a.nch)), dim3(nw * 64), 0, stream, a);
     return hipGetLastError();
 }
