@@ -161,8 +161,263 @@ __global__ __launch_bounds__(GT) void group_kernel(GroupArgs g, int nch)
     }
 }
 
+// Fast path for up to GT / 64 * TPW tiles of 64 pairs.  Each wave ranks the
+// pairs of its tiles among the lanes with the same expert id with one ballot
+// per key bit (the lanes whose key agrees on every bit are the same
+// expert), so a pair's rank within its tile is the number of lower lanes
+// among its peers, and the lowest peer writes the tile's count for that
+// expert.  A per-expert exclusive prefix over tiles, plus the expert
+// offsets, gives each pair its slot; the scatter is then one store per
+// pair.  Same result as the chunked kernel: pairs sorted by (expert, index).
+constexpr int TPW = 8;     // tiles per wave
+constexpr int KEYBITS = 11; // keys 0..1024: expert ids (at most 1024 experts), and
+                            // 1024 for "no expert"
+
+__global__ __launch_bounds__(GT) void group_tiles_kernel(GroupArgs g, int ntiles)
+{
+    extern __shared__ __align__(16) int32_t lds[];
+    const int E = g.n_experts, P = g.n_pairs, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    int32_t *hist = lds;                 // [ntiles][E]: counts, then prefix over tiles
+    int32_t *tot = hist + ntiles * E;    // [E]
+    int32_t *scan_a = tot + E;           // [GT] offsets scan
+    int32_t *scan_b = scan_a + GT;       // [GT] work-item scan
+    int32_t *wsum_a = scan_b + GT;       // [GT / 64] wave totals
+    int32_t *wsum_b = wsum_a + GT / 64;
+
+    for (int i = tid; i < ntiles * E; i += GT)
+        hist[i] = 0;
+    __syncthreads();
+
+    // 1. ranks within tiles and per-tile counts
+    int my_e[TPW], my_rank[TPW];
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        const int tile = wave + (GT / 64) * k;
+        const int p = tile * 64 + lane;
+        int e = -1;
+        if (tile < ntiles && p < P) {
+            e = g.ids[p];
+            if (e < 0 || e >= E)
+                e = -1;
+        }
+        const int key = e >= 0 ? e : 1024;
+        uint64_t peers = ~0ull;
+#pragma unroll
+        for (int b = 0; b < KEYBITS; ++b) {
+            const int bit = (key >> b) & 1;
+            const uint64_t bal = __ballot(bit);
+            peers &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(peers & ((1ull << lane) - 1));
+        if (e >= 0 && rank == 0)
+            hist[tile * E + e] = __popcll(peers);
+        my_e[k] = e;
+        my_rank[k] = rank;
+    }
+    __syncthreads();
+    // 2. per-expert exclusive prefix over tiles
+    for (int e = tid; e < E; e += GT) {
+        int run = 0;
+        for (int t = 0; t < ntiles; ++t) {
+            const int v = hist[t * E + e];
+            hist[t * E + e] = run;
+            run += v;
+        }
+        tot[e] = run;
+    }
+    __syncthreads();
+    // 3. inclusive scans over experts (E <= GT) of counts and work items
+    {
+        const int n = tid < E ? tot[tid] : 0;
+        int a = wave_inclusive_scan(n);
+        int b = wave_inclusive_scan((n + g.tpc - 1) / g.tpc);
+        if (lane == 63) {
+            wsum_a[wave] = a;
+            wsum_b[wave] = b;
+        }
+        __syncthreads();
+        for (int w = 0; w < wave; ++w) {
+            a += wsum_a[w];
+            b += wsum_b[w];
+        }
+        scan_a[tid] = a;
+        scan_b[tid] = b;
+        __syncthreads();
+    }
+    if (tid < E) {
+        const int excl = scan_a[tid] - tot[tid];
+        g.offsets[tid] = excl;
+        tot[tid] = excl; // reuse: start slot of expert tid
+    }
+    if (tid == 0) {
+        g.offsets[E] = scan_a[E - 1];
+        if (g.n_work)
+            *g.n_work = scan_b[E - 1];
+    }
+    __syncthreads();
+    // 4. scatter, one pair per lane and tile
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        const int tile = wave + (GT / 64) * k;
+        const int p = tile * 64 + lane;
+        if (tile >= ntiles || p >= P)
+            continue;
+        const int e = my_e[k];
+        if (e >= 0) {
+            const int s = tot[e] + hist[tile * E + e] + my_rank[k];
+            g.pair_of_slot[s] = p;
+            g.slot_of_pair[p] = s;
+            if (g.token_of_slot)
+                g.token_of_slot[s] = p / g.top_k;
+        } else {
+            g.slot_of_pair[p] = -1;
+        }
+    }
+    // 5. work items {expert, first slot, tokens, 0}
+    if (g.work && tid < E) {
+        const int n = scan_a[tid] - tot[tid];
+        const int first_item = scan_b[tid] - (n + g.tpc - 1) / g.tpc;
+        for (int c = 0; c * g.tpc < n; ++c) {
+            int4 wk;
+            wk.x = tid;
+            wk.y = tot[tid] + c * g.tpc;
+            wk.z = min(g.tpc, n - c * g.tpc);
+            wk.w = 0;
+            reinterpret_cast<int4 *>(g.work)[first_item + c] = wk;
+        }
+    }
+}
+
+// One wave, up to SMALL_TILES tiles of 64 pairs (decode-sized routing): the
+// same tile ranking, then the per-expert prefix and the scans over experts
+// in chunks of 64 experts, all within the wave.
+constexpr int SMALL_TILES = 8;
+
+__global__ __launch_bounds__(64) void group_small_kernel(GroupArgs g, int ntiles)
+{
+    extern __shared__ __align__(16) int32_t lds[];
+    const int E = g.n_experts, P = g.n_pairs, lane = threadIdx.x;
+    int32_t *hist = lds;              // [ntiles][E]
+    int32_t *cnt = hist + ntiles * E; // [E] pairs per expert
+    int32_t *start = cnt + E;         // [E] first slot
+    int32_t *item0 = start + E;       // [E] first work item
+
+    for (int i = lane; i < ntiles * E; i += 64)
+        hist[i] = 0;
+    __syncthreads();
+    int my_e[SMALL_TILES], my_rank[SMALL_TILES];
+#pragma unroll
+    for (int k = 0; k < SMALL_TILES; ++k) {
+        const int p = k * 64 + lane;
+        int e = -1;
+        if (k < ntiles && p < P) {
+            e = g.ids[p];
+            if (e < 0 || e >= E)
+                e = -1;
+        }
+        const int key = e >= 0 ? e : 1024;
+        uint64_t peers = ~0ull;
+#pragma unroll
+        for (int b = 0; b < KEYBITS; ++b) {
+            const int bit = (key >> b) & 1;
+            const uint64_t bal = __ballot(bit);
+            peers &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(peers & ((1ull << lane) - 1));
+        if (e >= 0 && rank == 0)
+            hist[k * E + e] = __popcll(peers);
+        my_e[k] = e;
+        my_rank[k] = rank;
+    }
+    __syncthreads();
+    for (int e = lane; e < E; e += 64) {
+        int run = 0;
+        for (int t = 0; t < ntiles; ++t) {
+            const int v = hist[t * E + e];
+            hist[t * E + e] = run;
+            run += v;
+        }
+        cnt[e] = run;
+    }
+    __syncthreads();
+    int carry_a = 0, carry_b = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        const int n = e < E ? cnt[e] : 0;
+        const int ni = (n + g.tpc - 1) / g.tpc;
+        const int a = wave_inclusive_scan(n) + carry_a;
+        const int b = wave_inclusive_scan(ni) + carry_b;
+        if (e < E) {
+            start[e] = a - n;
+            item0[e] = b - ni;
+            g.offsets[e] = a - n;
+        }
+        carry_a = __shfl(a, 63, 64);
+        carry_b = __shfl(b, 63, 64);
+    }
+    if (lane == 0) {
+        g.offsets[E] = carry_a;
+        if (g.n_work)
+            *g.n_work = carry_b;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < SMALL_TILES; ++k) {
+        const int p = k * 64 + lane;
+        if (k >= ntiles || p >= P)
+            continue;
+        const int e = my_e[k];
+        if (e >= 0) {
+            const int s = start[e] + hist[k * E + e] + my_rank[k];
+            g.pair_of_slot[s] = p;
+            g.slot_of_pair[p] = s;
+            if (g.token_of_slot)
+                g.token_of_slot[s] = p / g.top_k;
+        } else {
+            g.slot_of_pair[p] = -1;
+        }
+    }
+    if (g.work) {
+        for (int e = lane; e < E; e += 64) {
+            const int n = cnt[e];
+            for (int c = 0; c * g.tpc < n; ++c) {
+                int4 wk;
+                wk.x = e;
+                wk.y = start[e] + c * g.tpc;
+                wk.z = min(g.tpc, n - c * g.tpc);
+                wk.w = 0;
+                reinterpret_cast<int4 *>(g.work)[item0[e] + c] = wk;
+            }
+        }
+    }
+}
+
 hipError_t group_launch(const GroupArgs &g, hipStream_t stream)
 {
+    const int ntiles = (g.n_pairs + 63) / 64;
+    if (ntiles <= SMALL_TILES) {
+        const size_t slds = ((size_t)ntiles * g.n_experts + 3 * (size_t)g.n_experts) * 4;
+        // at most (8 + 3) * 1024 * 4 = 44 KB
+        hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(64), slds, stream, g, ntiles);
+        return hipGetLastError();
+    }
+    const size_t tlds =
+        ((size_t)ntiles * g.n_experts + g.n_experts + 2 * GT + 2 * (GT / 64)) * 4;
+    if (ntiles <= (GT / 64) * TPW && tlds <= 128 * 1024) {
+        static std::atomic<uint8_t> topted{0};
+        if (tlds > 64 * 1024 && !topted.load(std::memory_order_acquire)) {
+            hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void *>(group_tiles_kernel),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                160 * 1024);
+            if (st != hipSuccess)
+                return st;
+            topted.store(1, std::memory_order_release);
+        }
+        hipLaunchKernelGGL(group_tiles_kernel, dim3(1), dim3(GT), tlds, stream, g, ntiles);
+        return hipGetLastError();
+    }
+
     const int nch = group_chunks(g.n_pairs, g.n_experts);
     size_t lds = ((size_t)nch * g.n_experts + g.n_experts + 2 * GT + 2 * (GT / 64)) * 4;
     if (g.n_pairs <= IDS_IN_LDS)

@@ -174,13 +174,28 @@ def test_rerun_bitwise(m):
 
 
 def test_group_large(m, orc):
+    """All three grouping paths: one-wave tile ranking (up to 8 tiles of 64
+    pairs), 16-wave tile ranking (up to 128 tiles, histogram within 128 KB
+    of LDS) and chunked counting (beyond); 1024 experts; ids outside [0, E)
+    in a few cases."""
     rng = np.random.default_rng(45)
-    for (T, K, E) in [(512, 8, 256), (3000, 4, 1024), (1, 1, 1), (7, 32, 40)]:
+    for (T, K, E, bad) in [(512, 8, 256, 0), (3000, 4, 1024, 0), (1, 1, 1, 0), (7, 32, 40, 0),
+                           (1024, 8, 64, 0), (1024, 8, 512, 0), (20, 4, 1024, 0),
+                           (100, 6, 50, 9), (1100, 8, 300, 40), (64, 8, 1024, 5),
+                           (8, 6, 64, 0), (60, 8, 7, 3)]:
         ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+        if bad:
+            flat = ids.reshape(-1)
+            where = rng.choice(flat.size, bad, replace=False)
+            flat[where[: bad // 2]] = -1
+            flat[where[bad // 2:]] = E + 3
         offs, pos, slot = m.moe_route_group(dev(ids), E)
         counts, offs_o, pos_o, slot_o = orc.group(ids, E)
+        nv = int(offs_o[E])  # pairs with a valid expert; slots past them stay unwritten
+        hp = host(pos)
         assert np.array_equal(host(offs), offs_o)
-        assert np.array_equal(host(pos), pos_o)
+        assert np.array_equal(hp[:nv], pos_o[:nv])
+        assert np.all(hp[nv:] == -1)
         assert np.array_equal(host(slot), slot_o)
 
 
