@@ -58,6 +58,16 @@ def tensor_bytes(rows, cols):
     return rows * cols // 2 + rows * cols // 32
 
 
+def spread_us(timer, n):
+    """p10 / median / p90 of the per-launch time over ``n`` separately timed
+    graph replays, in us (empty in eager mode)."""
+    sp = timer.spread(n)
+    if sp is None:
+        return {}
+    return {"p10_us": round(sp[0] * 1e3, 3), "p50_us": round(sp[1] * 1e3, 3),
+            "p90_us": round(sp[2] * 1e3, 3)}
+
+
 class Timer:
     """Graph-replayed launches timed with HIP events on torch's stream."""
 
@@ -97,6 +107,24 @@ class Timer:
         if self.graph is not None:
             return (reps + self.passes - 1) // self.passes * self.passes * len(self.launches)
         return reps * len(self.launches)
+
+    def spread(self, n):
+        """Per-launch GPU ms of ``n`` separately timed graph replays (each one
+        pass count over the launch list): (p10, median, p90)."""
+        torch = self.torch
+        if self.graph is None:
+            return None
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record()
+            self.graph.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        per = sorted(e0.elapsed_time(e1) / (self.passes * len(self.launches)) for e0, e1 in ev)
+        q = lambda f: per[min(len(per) - 1, int(f * len(per)))]
+        return q(0.1), q(0.5), q(0.9)
 
     def time(self, reps):
         """Average GPU ms per launch over ``reps`` passes."""
@@ -261,10 +289,12 @@ def main():
     extra = {
         "gemm_4096x4096_b1": {"us": round(ms1 * 1e3, 3),
                               "weight_GBps": round(s1["nb"] / ms1 / 1e6, 1),
-                              "pct_peak": round(100 * s1["nb"] / ms1 / 1e6 / 8000, 1)},
+                              "pct_peak": round(100 * s1["nb"] / ms1 / 1e6 / 8000, 1),
+                              **spread_us(k1, 50)},
         "gemm_4096x4096_b8": {"us": round(ms8 * 1e3, 3),
                               "weight_GBps": round(s8["nb"] / ms8 / 1e6, 1),
-                              "pct_peak": round(100 * s8["nb"] / ms8 / 1e6 / 8000, 1)},
+                              "pct_peak": round(100 * s8["nb"] / ms8 / 1e6 / 8000, 1),
+                              **spread_us(k8, 50)},
     }
     for k, v in extra.items():
         log(f"{k}: {v}")
@@ -303,7 +333,8 @@ def main():
             gb = s["nb"] / ms / 1e6
             extra[f"gemm_14336x4096_b{b}"] = {"us": round(ms * 1e3, 3),
                                               "weight_GBps": round(gb, 1),
-                                              "pct_peak": round(100 * gb / 8000, 1)}
+                                              "pct_peak": round(100 * gb / 8000, 1),
+                                              **spread_us(t, 30)}
             log(f"gemm_14336x4096_b{b}: {extra[f'gemm_14336x4096_b{b}']}")
             del s, t
         torch.cuda.empty_cache()
@@ -317,22 +348,24 @@ def main():
                                    "touched_GB": round(s["touched"] / 1e9, 4),
                                    "active_experts": s["active"],
                                    "touched_GBps": round(s["touched"] / ms / 1e6, 1),
-                                   "pct_peak": round(100 * s["touched"] / ms / 1e6 / 8000, 1)}
+                                   "pct_peak": round(100 * s["touched"] / ms / 1e6 / 8000, 1),
+                                   **spread_us(t, 30)}
         log(f"moe_decode_e64: {extra['moe_decode_e64']}")
         del s, t
         torch.cuda.empty_cache()
     if "prefill" in sections:
         if True:
             s = moe_setup(torch, mx, inputs, 5, 1)
-            t = Timer(torch, s["launches"], args.eager)
-            ms = t.time(5)
+            t = Timer(torch, s["launches"], args.eager, passes=4)
+            ms = t.time(8)
             extra["moe_prefill_e256"] = {"us_per_layer": round(ms * 1e3, 2),
                                          "tok_per_s": round(s["T"] / (ms * 1e-3), 1),
                                          "touched_GB": round(s["touched"] / 1e9, 4),
                                          "active_experts": s["active"],
                                          "touched_GBps": round(s["touched"] / ms / 1e6, 1),
                                          "pct_peak": round(100 * s["touched"] / ms / 1e6 / 8000,
-                                                           1)}
+                                                           1),
+                                         **spread_us(t, 10)}
             log(f"moe_prefill_e256: {extra['moe_prefill_e256']}")
             del s, t
             torch.cuda.empty_cache()
