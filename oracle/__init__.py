@@ -69,6 +69,8 @@ def _load():
                                     P, P, P, P, P, ctypes.c_int]
     lib.orc_moe_down.restype = None
     lib.orc_moe_down.argtypes = [P, I64, I64, P, P, I64, I64, P, P, ctypes.c_int]
+    lib.orc_moe_v41_act.restype = None
+    lib.orc_moe_v41_act.argtypes = [P, P, P, P, I64, I64, ctypes.c_double, P]
     lib.orc_moe_combine.restype = None
     lib.orc_moe_combine.argtypes = [P, P, P, P, I64, I64, I64, P, P]
     _lib = lib
@@ -288,4 +290,55 @@ def moe(gate, up, down, n_experts, hidden, inter, x, topk_ids, topk_w, round_h_b
     y, mag_y = moe_down(down, n_experts, hidden, inter, st["h"], topk_ids, threads)
     out, mag_out = moe_combine(y, mag_y, topk_w, topk_ids, n_experts)
     st.update(y=y, mag_y=mag_y, out=out, mag_out=mag_out, out_bf16=bf16_rne_array(out).reshape(out.shape))
+    return st
+
+
+def moe_v41_act(g, u, topk_w, topk_ids, n_experts, swiglu_limit):
+    """V4.1 activation of every pair: h = bf16(w * silu(min(bf16 g, lim)) *
+    clamp(bf16 u, -lim, lim)) (no clamping when lim <= 0); [P, inter] fp64
+    holding bf16 values, pairs with invalid ids left at 0."""
+    ids = _sanitize_ids(topk_ids, n_experts)
+    T, K = ids.shape
+    P = T * K
+    g = np.ascontiguousarray(g, np.float64)
+    u = np.ascontiguousarray(u, np.float64)
+    assert g.shape == u.shape and g.shape[0] == P
+    inter = g.shape[1]
+    w = np.ascontiguousarray(topk_w, np.float64).reshape(P)
+    h = np.zeros((P, inter), np.float64)
+    _load().orc_moe_v41_act(_ptr(g), _ptr(u), _ptr(w), _ptr(ids), P, inter,
+                            float(swiglu_limit), _ptr(h))
+    return h
+
+
+def v41_routing(topk_ids, topk_w, n_experts, has_shared):
+    """Routing with the shared expert as one more slot per token: expert
+    n_experts with weight 1 (the banks then hold n_experts + 1 experts)."""
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    if not has_shared:
+        return ids, w, n_experts
+    T = ids.shape[0]
+    ids2 = np.concatenate([ids, np.full((T, 1), n_experts, np.int32)], axis=1)
+    w2 = np.concatenate([w, np.ones((T, 1), np.float32)], axis=1)
+    return ids2, w2, n_experts + 1
+
+
+def moe_v41(gate, up, down, n_experts, hidden, inter, x, topk_ids, topk_w, swiglu_limit,
+            has_shared, threads=None):
+    """The V4.1 expert bank: per pair, exact gate/up products, the V4.1
+    activation (bf16 gate/up, limit, route weight folded, bf16 h), the down
+    product, then out[t] = sum over the token's slots of the down outputs
+    (no further weighting), rounded once to bf16 ("cortiq-engine 0.8.40,
+    src/gpu_wgpu/mxfp4.rs": dsv4_global_down_mxfp4 with its bf16 flag sums
+    every slot of a token in one reduction).  With has_shared, expert
+    n_experts is applied to every token with weight 1."""
+    ids, w, E = v41_routing(topk_ids, topk_w, n_experts, has_shared)
+    st = moe_gate_up(gate, up, E, hidden, inter, x, ids, False, threads)
+    h = moe_v41_act(st["g"], st["u"], w, ids, E, swiglu_limit)
+    y, mag_y = moe_down(down, E, hidden, inter, h, ids, threads)
+    ones = np.ones(ids.shape, np.float64)
+    out, mag_out = moe_combine(y, mag_y, ones, ids, E)
+    st.update(h=h, y=y, mag_y=mag_y, out=out, mag_out=mag_out,
+              out_bf16=bf16_rne_array(out).reshape(out.shape), ids=ids, w=w, n_experts=E)
     return st

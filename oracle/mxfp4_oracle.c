@@ -443,6 +443,45 @@ void orc_moe_down(const uint8_t *down, int64_t hidden, int64_t inter, const doub
     run_moe(j, nthreads);
 }
 
+/* bf16 value (RNE) of an fp64 number, back as fp64. */
+static double bf16_value(double v)
+{
+    uint32_t bits = (uint32_t)orc_bf16_rne(v) << 16;
+    float f;
+    memcpy(&f, &bits, 4);
+    return f;
+}
+
+/* V4.1 expert activation of every pair ("cortiq-engine 0.8.40,
+ * src/gpu_wgpu/mxfp4.rs": dsv4_global_gate_up_mxfp4 with its bf16 flag,
+ * and the host expert of global_bank_case): gate and up are rounded to
+ * bf16; with a limit lim > 0 up is clamped to [-lim, lim] and gate capped
+ * at lim (gate has no lower bound); act = silu(gate) * up; the pair's
+ * route weight is folded in and the product rounded to bf16:
+ * h = bf16(w * act).  g, u: the exact gate/up products [n_pairs][inter];
+ * pairs with ids < 0 are skipped (h left untouched).
+ * Parity pinned by: test_oracle_v41.py (exact-bf16 gate/up reduce it to the
+ * pinned bf16 SwiGLU; limit cases worked by hand; power-of-two route
+ * weights scale h exactly; two half-weight slots of one expert equal one
+ * full-weight slot; the shared slot equals explicit routing). */
+void orc_moe_v41_act(const double *g, const double *u, const double *w, const int32_t *ids,
+                     int64_t n_pairs, int64_t inter, double lim, double *h)
+{
+    for (int64_t p = 0; p < n_pairs; ++p) {
+        if (ids[p] < 0)
+            continue;
+        for (int64_t r = 0; r < inter; ++r) {
+            double gb = bf16_value(g[p * inter + r]);
+            double ub = bf16_value(u[p * inter + r]);
+            if (lim > 0) {
+                ub = ub < -lim ? -lim : (ub > lim ? lim : ub);
+                gb = gb > lim ? lim : gb;
+            }
+            h[p * inter + r] = bf16_value(w[p] * (silu(gb) * ub));
+        }
+    }
+}
+
 /* Weighted sum over each token's slots in slot order:
  * out[t] = sum_k w[t][k] * y[t*top_k + k], with the weight applied to the
  * down output ([wgpu] dsv4_global_down_mxfp4, generic f32 weighting), and
