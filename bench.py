@@ -152,7 +152,7 @@ def gemm_setup(torch, mx, inputs, rows, cols, b, seed, pool_bytes=POOL_BYTES):
                 alg_bytes=nb + b * cols * 4 + b * rows * 4)
 
 
-def moe_setup(torch, mx, inputs, wl, banks):
+def moe_setup(torch, mx, inputs, wl, banks, extra_experts=0):
     import numpy as np
     cfg = inputs.WORKLOADS[wl]
     E, H, I, T, K = (cfg["n_experts"], cfg["hidden"], cfg["inter"], cfg["n_tokens"],
@@ -167,7 +167,8 @@ def moe_setup(torch, mx, inputs, wl, banks):
     for j in range(banks):
         s = 100 * wl + 10 * j
         bank.append([inputs.draw_weights_device(s + r, I if r < 2 else H, H if r < 2 else I,
-                                                cfg["scale_lo"], cfg["scale_hi"], E)
+                                                cfg["scale_lo"], cfg["scale_hi"],
+                                                E + extra_experts)
                      for r in range(3)])
     g = torch.Generator(device="cuda")
     g.manual_seed(wl)
@@ -368,6 +369,29 @@ def main():
                                          **spread_us(t, 10)}
             log(f"moe_prefill_e256: {extra['moe_prefill_e256']}")
             del s, t
+            torch.cuda.empty_cache()
+            # the same layer in V4.1 form: bf16 gate/up, SwiGLU limit 10, route
+            # weight folded into h, plus a shared expert on every token
+            s = moe_setup(torch, mx, inputs, 5, 1, extra_experts=1)
+            cfg = inputs.WORKLOADS[5]
+            E, H, I = cfg["n_experts"], cfg["hidden"], cfg["inter"]
+            ws = torch.empty(mx.moe_experts_mxfp4_v41_workspace_size(s["T"], cfg["top_k"], E, H, I,
+                                                                     True),
+                             dtype=torch.uint8, device="cuda")
+            bk = s["bank"][0]
+            L = [lambda: mx.moe_experts_mxfp4_v41(bk[0], bk[1], bk[2], E, H, I, s["x"], s["ids"],
+                                                  s["w"], swiglu_limit=10.0, has_shared=True,
+                                                  out=s["out"], workspace=ws)]
+            t = Timer(torch, L, args.eager, passes=4)
+            ms = t.time(8)
+            touched = s["touched"] + 3 * tensor_bytes(I, H)
+            extra["moe_prefill_e256_v41_shared"] = {
+                "us_per_layer": round(ms * 1e3, 2), "tok_per_s": round(s["T"] / (ms * 1e-3), 1),
+                "touched_GB": round(touched / 1e9, 4),
+                "touched_GBps": round(touched / ms / 1e6, 1),
+                "pct_peak": round(100 * touched / ms / 1e6 / 8000, 1), **spread_us(t, 10)}
+            log(f"moe_prefill_e256_v41_shared: {extra['moe_prefill_e256_v41_shared']}")
+            del s, t, L, ws
             torch.cuda.empty_cache()
     if "cpu" in sections:
         cpu = cpu_baseline(args.cpu_seconds)

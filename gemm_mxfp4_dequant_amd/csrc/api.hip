@@ -95,7 +95,8 @@ constexpr int TILED_MIN_WGS = 192; // GEMM: tiled only with ~one workgroup per C
 
 // Workspace layout of the expert bank.
 struct MoeLayout {
-    size_t offsets, pair_of_slot, slot_of_pair, token_of_slot, work, n_work, h, y, total;
+    size_t offsets, pair_of_slot, slot_of_pair, token_of_slot, work, n_work, h, y, ids_aug, w_aug,
+        total;
 };
 
 MoeLayout moe_layout(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t hidden,
@@ -120,9 +121,23 @@ MoeLayout moe_layout(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t
     o += align256((size_t)P * inter * (x_dtype == MXFP4_BF16 ? 2 : 4));
     L.y = o;
     o += align256((size_t)P * hidden * 4);
+    L.ids_aug = o; // routing with a shared expert (V4.1)
+    o += align256((size_t)P * 4);
+    L.w_aug = o;
+    o += align256((size_t)P * 4);
     L.total = o;
     return L;
 }
+
+// Expert-bank variants: the plain bank (route weight on the fp32 down
+// output) or the V4.1 bank (bf16 gate/up, SwiGLU limit, route weight folded
+// into the bf16 activation, slots summed unweighted, optional shared expert
+// applied to every token as slot top_k with weight 1).
+struct MoeMode {
+    bool v41;
+    float lim;
+    bool shared;
+};
 
 int check_moe(const void *gate, const void *up, const void *down, int64_t n_experts,
               int64_t hidden, int64_t inter, const void *x, int x_dtype, int64_t n_tokens,
@@ -166,12 +181,25 @@ int check_moe(const void *gate, const void *up, const void *down, int64_t n_expe
 int moe_run(const void *gate, const void *up, const void *down, int64_t n_experts, int64_t hidden,
             int64_t inter, const void *x, int x_dtype, int64_t n_tokens, const int32_t *topk_ids,
             const float *topk_w, int64_t top_k, void *out, int out_dtype, void *workspace,
-            const void *h_in, void *h_out, hipStream_t st)
+            const void *h_in, void *h_out, const MoeMode &mode, hipStream_t st)
 {
     const bool xbf = x_dtype == MXFP4_BF16;
-    const int P = (int)(n_tokens * top_k);
-    const MoeLayout L = moe_layout(n_tokens, top_k, n_experts, hidden, inter, x_dtype);
+    const MoeLayout L = moe_layout(n_tokens, top_k + mode.shared, n_experts + mode.shared, hidden,
+                                   inter, x_dtype);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
+    if (mode.shared) {
+        // the shared expert becomes slot top_k of every token
+        int32_t *ids_aug = reinterpret_cast<int32_t *>(ws + L.ids_aug);
+        float *w_aug = reinterpret_cast<float *>(ws + L.w_aug);
+        TRY(launched(mx::augment_launch(topk_ids, topk_w, (int)n_tokens, (int)top_k,
+                                        (int)n_experts, ids_aug, w_aug, st),
+                     "shared-expert routing"));
+        topk_ids = ids_aug;
+        topk_w = w_aug;
+        top_k += 1;
+        n_experts += 1;
+    }
+    const int P = (int)(n_tokens * top_k);
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
     int32_t *pos = reinterpret_cast<int32_t *>(ws + L.pair_of_slot);
     int32_t *slot = reinterpret_cast<int32_t *>(ws + L.slot_of_pair);
@@ -238,6 +266,10 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
         a.work = work;
         a.n_work = n_work;
         a.token_of_slot = tos;
+        a.v41 = mode.v41;
+        a.lim = mode.lim;
+        a.pair_of_slot = pos;
+        a.pair_w = topk_w;
         if (tiled) {
             TRY(launched(mx::tiled_launch(mx::MODE_GATEUP, xbf, TILED_NW_MOE, TILED_RT_GATEUP,
                                           TILED_NC, a, st),
@@ -275,8 +307,9 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
             TRY(launched(mx::skinny_launch(mx::MODE_DOWN, xbf, sh, a, st), "down"));
         }
     }
-    TRY(launched(mx::combine_launch(y, slot, topk_w, (int)n_tokens, (int)top_k, (int)hidden, out,
-                                    out_dtype == MXFP4_BF16, st),
+    // V4.1: the route weights are already in h; the slots are summed as they are
+    TRY(launched(mx::combine_launch(y, slot, mode.v41 ? nullptr : topk_w, (int)n_tokens,
+                                    (int)top_k, (int)hidden, out, out_dtype == MXFP4_BF16, st),
                  "combine"));
     return MXFP4_OK;
 }
@@ -420,7 +453,7 @@ int moe_experts_mxfp4(const void *gate, const void *up, const void *down, int64_
     TRY(check_moe(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
                   topk_w, top_k, out, out_dtype, true, workspace, workspace_bytes));
     return moe_run(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
-                   topk_w, top_k, out, out_dtype, workspace, nullptr, nullptr,
+                   topk_w, top_k, out, out_dtype, workspace, nullptr, nullptr, MoeMode{},
                    (hipStream_t)stream);
 }
 
@@ -443,7 +476,77 @@ int moe_experts_mxfp4_stages(const void *gate, const void *up, const void *down,
     if (h_in && h_out)
         return fail(MXFP4_EINVAL, "stages: h_in and h_out are exclusive");
     return moe_run(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
-                   topk_w, top_k, out, out_dtype, workspace, h_in, h_out, (hipStream_t)stream);
+                   topk_w, top_k, out, out_dtype, workspace, h_in, h_out, MoeMode{},
+                   (hipStream_t)stream);
+}
+
+size_t moe_experts_mxfp4_v41_workspace_size(int64_t n_tokens, int64_t top_k, int64_t n_experts,
+                                            int64_t hidden, int64_t inter, int has_shared)
+{
+    if (has_shared != 0 && has_shared != 1)
+        return 0;
+    return moe_experts_mxfp4_workspace_size(n_tokens, top_k + has_shared, n_experts + has_shared,
+                                            hidden, inter, MXFP4_BF16);
+}
+
+namespace {
+
+int check_v41(const void *gate, const void *up, const void *down, int64_t n_experts,
+              int64_t hidden, int64_t inter, const void *x, int64_t n_tokens,
+              const int32_t *topk_ids, const float *topk_w, int64_t top_k, float swiglu_limit,
+              int has_shared, void *out, bool need_out, void *workspace, size_t workspace_bytes)
+{
+    if (has_shared != 0 && has_shared != 1)
+        return fail(MXFP4_EINVAL, "has_shared = %d is not 0 or 1", has_shared);
+    if (!(swiglu_limit >= 0.0f) || swiglu_limit > 3.0e38f)
+        return fail(MXFP4_EINVAL, "swiglu_limit must be finite and >= 0 (0: no limit)");
+    if (top_k < 1 || top_k > n_experts)
+        return fail(MXFP4_EINVAL, "top_k = %lld outside [1, n_experts]", (long long)top_k);
+    // the grouping and kernels see top_k + has_shared slots over
+    // n_experts + has_shared experts
+    TRY(check_moe(gate, up, down, n_experts + has_shared, hidden, inter, x, MXFP4_BF16, n_tokens,
+                  topk_ids, topk_w, top_k + has_shared, out, MXFP4_BF16, need_out, workspace,
+                  workspace_bytes));
+    return MXFP4_OK;
+}
+
+} // namespace
+
+int moe_experts_mxfp4_v41(const void *gate, const void *up, const void *down, int64_t n_experts,
+                          int64_t hidden, int64_t inter, const void *x, int64_t n_tokens,
+                          const int32_t *topk_ids, const float *topk_w, int64_t top_k,
+                          float swiglu_limit, int has_shared, void *out, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    clear_error();
+    TRY(check_v41(gate, up, down, n_experts, hidden, inter, x, n_tokens, topk_ids, topk_w, top_k,
+                  swiglu_limit, has_shared, out, true, workspace, workspace_bytes));
+    return moe_run(gate, up, down, n_experts, hidden, inter, x, MXFP4_BF16, n_tokens, topk_ids,
+                   topk_w, top_k, out, MXFP4_BF16, workspace, nullptr, nullptr,
+                   MoeMode{true, swiglu_limit, has_shared != 0}, (hipStream_t)stream);
+}
+
+int moe_experts_mxfp4_v41_stages(const void *gate, const void *up, const void *down,
+                                 int64_t n_experts, int64_t hidden, int64_t inter, const void *x,
+                                 int64_t n_tokens, const int32_t *topk_ids, const float *topk_w,
+                                 int64_t top_k, float swiglu_limit, int has_shared, void *out,
+                                 void *workspace, size_t workspace_bytes, const void *h_in,
+                                 void *h_out, void *stream)
+{
+    clear_error();
+    TRY(check_v41(gate, up, down, n_experts, hidden, inter, x, n_tokens, topk_ids, topk_w, top_k,
+                  swiglu_limit, has_shared, out, out != nullptr, workspace, workspace_bytes));
+    if (!out && !h_out)
+        return fail(MXFP4_EINVAL, "stages: nothing requested (out and h_out are both null)");
+    if (h_in)
+        TRY(check_buffer("h_in", h_in, 16));
+    if (h_out)
+        TRY(check_buffer("h_out", h_out, 16));
+    if (h_in && h_out)
+        return fail(MXFP4_EINVAL, "stages: h_in and h_out are exclusive");
+    return moe_run(gate, up, down, n_experts, hidden, inter, x, MXFP4_BF16, n_tokens, topk_ids,
+                   topk_w, top_k, out, MXFP4_BF16, workspace, h_in, h_out,
+                   MoeMode{true, swiglu_limit, has_shared != 0}, (hipStream_t)stream);
 }
 
 } // extern "C"

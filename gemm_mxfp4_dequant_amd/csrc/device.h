@@ -99,6 +99,21 @@ __device__ __forceinline__ float dpp_row_ror8(float v)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// V4.1 expert activation ("cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs",
+// dsv4_global_gate_up_mxfp4 with its bf16 flag): gate and up rounded to
+// bf16; with lim > 0 up clamped to [-lim, lim] and gate capped at lim; the
+// route weight w folded in.  The caller rounds the result to bf16.
+__device__ __forceinline__ float swiglu_v41(float g, float u, float w, float lim)
+{
+    g = bf16_bits_to_f32(f32_to_bf16_bits(g));
+    u = bf16_bits_to_f32(f32_to_bf16_bits(u));
+    if (lim > 0.0f) {
+        u = u < -lim ? -lim : (u > lim ? lim : u);
+        g = g > lim ? lim : g;
+    }
+    return w * (silu(g) * u);
+}
+
 constexpr int NXCD = 8; // MI355X: 8 XCDs, each with its own L2
 
 // Workgroups are dispatched to the XCDs round-robin by id.  This maps the

@@ -25,6 +25,13 @@ struct SkinnyArgs {
     const int *work;          // MoE: int4 {expert, first slot, tokens, 0} per item
     const int *n_work;        // MoE: number of items (device)
     const int *token_of_slot; // GATEUP: token row of each slot
+    // GATEUP, V4.1 activation (v41 != 0): h = bf16(w * silu(min(bf16 g, lim)) *
+    // clamp(bf16 u, -lim, lim)), clamping only when lim > 0; w = pair_w of the
+    // slot's pair
+    int v41;
+    float lim;
+    const int *pair_of_slot;
+    const float *pair_w;
 };
 
 // Launch shape of one skinny call: K slab width (0 = generic kernel),
@@ -71,7 +78,12 @@ struct GroupArgs {
 hipError_t group_launch(const GroupArgs &g, hipStream_t stream);
 int group_max_work(int n_pairs, int n_experts, int tpc);
 
-// out[t][r] = sum_k w[t][k] * y[slot_of_pair[t*K+k]][r]
+// V4.1 routing with a shared expert: ids_aug[t][k] = ids[t][k] for k < K
+// (ids outside [0, E) become -1) and E for k = K; w_aug likewise with 1.
+hipError_t augment_launch(const int32_t *ids, const float *w, int n_tokens, int top_k,
+                          int n_experts, int32_t *ids_aug, float *w_aug, hipStream_t stream);
+
+// out[t][r] = sum_k w[t][k] * y[slot_of_pair[t*K+k]][r] (w == nullptr: unit weights)
 hipError_t combine_launch(const float *y, const int32_t *slot_of_pair, const float *w,
                           int n_tokens, int top_k, int hidden, void *out, bool out_bf16,
                           hipStream_t stream);

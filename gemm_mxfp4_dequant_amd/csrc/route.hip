@@ -10,7 +10,9 @@
 //
 // The combine is the weighted sum of "cortiq-engine 0.8.40,
 // src/gpu_wgpu/mxfp4.rs" (dsv4_global_down_mxfp4, generic f32 weighting:
-// the route weight multiplies the fp32 down output), summed in slot order
+// the route weight multiplies the fp32 down output; in V4.1 mode the weight
+// is already folded into the activation and the slots are summed as they
+// are), summed in slot order
 // k = 0..top_k-1, and the un-permutation of "rlx-cpu 0.2.17,
 // src/gguf_matmul.rs" (grouped_moe_unpermute_out); bf16 output is rounded
 // to nearest-even (the mxg_bf16 rule).
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *y, const int3
             const int k = k0 + j;
             const int s = k < top_k ? slot_of_pair[t * top_k + k] : -1;
             ok[j] = s >= 0;
-            wk[j] = ok[j] ? w[t * top_k + k] : 0.f;
+            wk[j] = ok[j] ? (w ? w[t * top_k + k] : 1.f) : 0.f;
             v[j] = ok[j] ? *reinterpret_cast<const f32x4 *>(y + (int64_t)s * hidden + r)
                          : f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -476,6 +478,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *y, const int3
     } else {
         *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + (int64_t)t * hidden + r) = acc;
     }
+}
+
+// V4.1 routing with the shared expert as slot K of every token (expert E,
+// weight 1); routed ids outside [0, E) become -1 so that none can alias the
+// shared expert.
+__global__ __launch_bounds__(256) void augment_kernel(const int32_t *ids, const float *w, int n,
+                                                      int top_k, int n_experts, int32_t *ids_aug,
+                                                      float *w_aug)
+{
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= n)
+        return;
+    const int t = p / (top_k + 1), k = p % (top_k + 1);
+    if (k < top_k) {
+        const int e = ids[t * top_k + k];
+        ids_aug[p] = (e >= 0 && e < n_experts) ? e : -1;
+        w_aug[p] = w[t * top_k + k];
+    } else {
+        ids_aug[p] = n_experts;
+        w_aug[p] = 1.0f;
+    }
+}
+
+hipError_t augment_launch(const int32_t *ids, const float *w, int n_tokens, int top_k,
+                          int n_experts, int32_t *ids_aug, float *w_aug, hipStream_t stream)
+{
+    const int n = n_tokens * (top_k + 1);
+    hipLaunchKernelGGL(augment_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       ids, w, n, top_k, n_experts, ids_aug, w_aug);
+    return hipGetLastError();
 }
 
 hipError_t combine_launch(const float *y, const int32_t *slot_of_pair, const float *w,

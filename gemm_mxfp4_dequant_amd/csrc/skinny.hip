@@ -179,6 +179,7 @@ __device__ __forceinline__ void store_tile(const SkinnyArgs &a, const TileMap &t
     const int R = a.rows;
     const int rbase = tm.row0 + tile * 16 + 4 * ls;
     const int64_t orow = tm.slot0 + li; // token (GEMM) or slot (MoE)
+    const float pw = (MODE == MODE_GATEUP && a.v41) ? a.pair_w[a.pair_of_slot[orow]] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = rbase + i;
@@ -186,7 +187,7 @@ __device__ __forceinline__ void store_tile(const SkinnyArgs &a, const TileMap &t
             continue;
         float v = g[i];
         if (MODE == MODE_GATEUP)
-            v = silu(g[i]) * u[i];
+            v = a.v41 ? swiglu_v41(g[i], u[i], pw, a.lim) : silu(g[i]) * u[i];
         if (MODE != MODE_DOWN && a.y_bf16)
             reinterpret_cast<uint16_t *>(a.y)[orow * R + r] = f32_to_bf16_bits(v);
         else

@@ -335,6 +335,8 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
                 continue;
             const int rbase = row0 + (wave * RT + rt) * 16 + 4 * ls;
             const int64_t orow = slot0 + tok;
+            const float pw =
+                (MODE == MODE_GATEUP && a.v41) ? a.pair_w[a.pair_of_slot[orow]] : 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rbase + i;
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
                     continue;
                 float v = g[i];
                 if (MODE == MODE_GATEUP)
-                    v = silu(g[i]) * u[i];
+                    v = a.v41 ? swiglu_v41(g[i], u[i], pw, a.lim) : silu(g[i]) * u[i];
                 if (MODE != MODE_DOWN && a.y_bf16)
                     reinterpret_cast<uint16_t *>(a.y)[orow * R + r] = f32_to_bf16_bits(v);
                 else

@@ -53,6 +53,12 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_size_t, P]),
         "moe_experts_mxfp4_stages": (I, [P, P, P, I64, I64, I64, P, I, I64, P, P, I64, P, I,
                                          P, ctypes.c_size_t, P, P, P]),
+        "moe_experts_mxfp4_v41_workspace_size": (ctypes.c_size_t, [I64, I64, I64, I64, I64, I]),
+        "moe_experts_mxfp4_v41": (I, [P, P, P, I64, I64, I64, P, I64, P, P, I64,
+                                      ctypes.c_float, I, P, P, ctypes.c_size_t, P]),
+        "moe_experts_mxfp4_v41_stages": (I, [P, P, P, I64, I64, I64, P, I64, P, P, I64,
+                                             ctypes.c_float, I, P, P, ctypes.c_size_t, P, P,
+                                             P]),
         "mxfp4_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -178,4 +184,46 @@ def moe_experts_mxfp4_stages(gate, up, down, n_experts, hidden, inter, x, topk_i
                                           inter, _ptr(x), _dt(x), T, _ptr(topk_ids),
                                           _ptr(topk_w), K, _ptr(out), out_code, _ptr(ws),
                                           ws_bytes, _ptr(h_in), _ptr(h_out), _stream(stream)))
+    return out, h_out
+
+
+def moe_experts_mxfp4_v41_workspace_size(n_tokens, top_k, n_experts, hidden, inter,
+                                         has_shared) -> int:
+    return int(lib().moe_experts_mxfp4_v41_workspace_size(n_tokens, top_k, n_experts, hidden,
+                                                          inter, int(has_shared)))
+
+
+def _v41_ws(workspace, T, K, E, H, I, has_shared, dev):
+    need = moe_experts_mxfp4_v41_workspace_size(T, K, E, H, I, has_shared)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def moe_experts_mxfp4_v41(gate, up, down, n_experts, hidden, inter, x, topk_ids, topk_w,
+                          swiglu_limit=0.0, has_shared=False, out=None, workspace=None,
+                          stream=None):
+    """V4.1 expert bank (bf16 x and out); with has_shared the banks hold
+    n_experts + 1 experts, the shared one last."""
+    T, K = topk_ids.shape
+    if out is None:
+        out = torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
+    ws, ws_bytes = _v41_ws(workspace, T, K, n_experts, hidden, inter, has_shared, x.device)
+    _check(lib().moe_experts_mxfp4_v41(_ptr(gate), _ptr(up), _ptr(down), n_experts, hidden,
+                                       inter, _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), K,
+                                       float(swiglu_limit), int(has_shared), _ptr(out), _ptr(ws),
+                                       ws_bytes, _stream(stream)))
+    return out
+
+
+def moe_experts_mxfp4_v41_stages(gate, up, down, n_experts, hidden, inter, x, topk_ids, topk_w,
+                                 swiglu_limit=0.0, has_shared=False, out=None, workspace=None,
+                                 h_in=None, h_out=None, stream=None):
+    T, K = topk_ids.shape
+    ws, ws_bytes = _v41_ws(workspace, T, K, n_experts, hidden, inter, has_shared, x.device)
+    _check(lib().moe_experts_mxfp4_v41_stages(_ptr(gate), _ptr(up), _ptr(down), n_experts,
+                                              hidden, inter, _ptr(x), T, _ptr(topk_ids),
+                                              _ptr(topk_w), K, float(swiglu_limit),
+                                              int(has_shared), _ptr(out), _ptr(ws), ws_bytes,
+                                              _ptr(h_in), _ptr(h_out), _stream(stream)))
     return out, h_out

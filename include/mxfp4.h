@@ -140,6 +140,42 @@ int moe_experts_mxfp4_stages(const void *gate, const void *up, const void *down,
                              void *workspace, size_t workspace_bytes, const void *h_in,
                              void *h_out, void *stream);
 
+/* V4.1 expert bank ("cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs":
+ * dsv4_global_gate_up_mxfp4 and dsv4_global_down_mxfp4 with their bf16
+ * flag, and the host expert of global_bank_case).  x and out are bf16.  For
+ * each routed pair p = (t, k), e = topk_ids[p], w = topk_w[p]:
+ *     g = bf16(W_gate[e] x_t),  u = bf16(W_up[e] x_t)   (fp32 products rounded)
+ *     if swiglu_limit > 0:  u = clamp(u, -limit, limit),  g = min(g, limit)
+ *     h_p = bf16(w * (silu(g) * u))                     (route weight folded in)
+ *     out[t] = bf16(sum over the token's slots of W_down[e] h_p)   (no weight)
+ * swiglu_limit: finite, >= 0; 0 means no limit.  has_shared = 1 applies one
+ * more expert, index n_experts, to every token with weight 1 as slot top_k:
+ * gate, up and down then hold n_experts + 1 tensors each, the shared one
+ * last.  Ids outside [0, n_experts) drop the pair (they never select the
+ * shared expert).  Summation order and accumulation as in moe_experts_mxfp4;
+ * the down outputs of a token's slots are summed in slot order in fp32 and
+ * rounded once.  Workspace: at least moe_experts_mxfp4_v41_workspace_size
+ * bytes (device, 16-byte aligned, scratch owned by the call until the stream
+ * reaches it).  Errors as moe_experts_mxfp4; also MXFP4_EINVAL for a
+ * negative or non-finite limit or has_shared outside {0, 1}. */
+size_t moe_experts_mxfp4_v41_workspace_size(int64_t n_tokens, int64_t top_k, int64_t n_experts,
+                                            int64_t hidden, int64_t inter, int has_shared);
+int moe_experts_mxfp4_v41(const void *gate, const void *up, const void *down, int64_t n_experts,
+                          int64_t hidden, int64_t inter, const void *x, int64_t n_tokens,
+                          const int32_t *topk_ids, const float *topk_w, int64_t top_k,
+                          float swiglu_limit, int has_shared, void *out, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Stage-isolation variant of moe_experts_mxfp4_v41, as
+ * moe_experts_mxfp4_stages: h in SLOT order, bf16,
+ * [n_tokens * (top_k + has_shared)][inter]. */
+int moe_experts_mxfp4_v41_stages(const void *gate, const void *up, const void *down,
+                                 int64_t n_experts, int64_t hidden, int64_t inter, const void *x,
+                                 int64_t n_tokens, const int32_t *topk_ids, const float *topk_w,
+                                 int64_t top_k, float swiglu_limit, int has_shared, void *out,
+                                 void *workspace, size_t workspace_bytes, const void *h_in,
+                                 void *h_out, void *stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *mxfp4_last_error(void);
 

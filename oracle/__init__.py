@@ -313,8 +313,10 @@ def moe_v41_act(g, u, topk_w, topk_ids, n_experts, swiglu_limit):
 
 def v41_routing(topk_ids, topk_w, n_experts, has_shared):
     """Routing with the shared expert as one more slot per token: expert
-    n_experts with weight 1 (the banks then hold n_experts + 1 experts)."""
-    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    n_experts with weight 1 (the banks then hold n_experts + 1 experts).
+    Routed ids outside [0, n_experts) drop their pair and never select the
+    shared expert."""
+    ids = _sanitize_ids(topk_ids, n_experts)
     w = np.ascontiguousarray(topk_w, dtype=np.float32)
     if not has_shared:
         return ids, w, n_experts

@@ -36,7 +36,7 @@ def m():
 
 def test_exports_every_declared_symbol(m):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     L = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(L, n), n
@@ -117,6 +117,31 @@ def test_moe_refusals(m):
     assert call(ids=FAKE + 2) == m.MXFP4_EALIGN
     assert call(xdt=5) == m.MXFP4_EINVAL
     assert args
+
+
+def test_v41_refusals(m):
+    """The V4.1 bank refuses a negative or non-finite limit, has_shared
+    outside {0, 1}, and a workspace sized without the shared expert's slot."""
+    L = m.lib()
+    ws0 = m.moe_experts_mxfp4_v41_workspace_size(16, 8, 256, 1024, 512, 0)
+    ws1 = m.moe_experts_mxfp4_v41_workspace_size(16, 8, 256, 1024, 512, 1)
+    assert ws1 > ws0 > 0
+    assert m.moe_experts_mxfp4_v41_workspace_size(16, 8, 256, 1024, 512, 2) == 0
+
+    def call(lim=10.0, shared=1, ws_bytes=ws1, K=8, E=256):
+        return L.moe_experts_mxfp4_v41(FAKE, FAKE, FAKE, E, 1024, 512, FAKE, 16, FAKE, FAKE, K,
+                                       lim, shared, FAKE, FAKE, ws_bytes, None)
+
+    assert call(lim=-1.0) == m.MXFP4_EINVAL
+    assert call(lim=float("nan")) == m.MXFP4_EINVAL
+    assert call(lim=float("inf")) == m.MXFP4_EINVAL
+    assert call(shared=2) == m.MXFP4_EINVAL
+    assert call(ws_bytes=ws0) == m.MXFP4_EWORKSPACE   # no room for the shared slot
+    assert call(K=257) == m.MXFP4_EINVAL
+    assert call(K=32, E=256) == m.MXFP4_EINVAL         # 32 routed + 1 shared > 32 slots
+    r = L.moe_experts_mxfp4_v41_stages(FAKE, FAKE, FAKE, 256, 1024, 512, FAKE, 16, FAKE, FAKE, 8,
+                                       10.0, 1, None, FAKE, ws1, None, None, None)
+    assert r == m.MXFP4_EINVAL                          # nothing requested
 
 
 def test_stage_refusals(m):

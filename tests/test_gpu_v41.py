@@ -1,0 +1,167 @@
+"""GPU parity of the V4.1 expert bank (moe_experts_mxfp4_v41) against the
+oracle: bf16 gate/up, SwiGLU limit, route weight folded into the bf16
+activation, slots summed unweighted and rounded once, optional shared
+expert ("cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs": dsv4_global_gate_up_
+mxfp4 / dsv4_global_down_mxfp4 with their bf16 flag, and the host expert of
+global_bank_case).
+
+* stage isolation, h (slot order) against the oracle's h:
+    |h_gpu - h_or| <= |w| (1.1 dg |u_b| + |silu(g_b)| du) + 1 ulp_bf16(h_or)
+  with dg = 1e-4 mag_g + ulp_bf16(g), du = 1e-4 mag_u + ulp_bf16(u): the
+  library's product rule plus one bf16 step of g or u (both sides round
+  their own sums to bf16), through silu (|silu'| < 1.1) and the clamp
+  (1-Lipschitz), then h's own rounding;
+* down + combine fed with h_gpu:
+    |out_gpu - out_or| <= 1e-4 sum_k mag_y + 1 ulp_bf16(out_or);
+* end to end: nrmse < 2e-3 and cosine > 0.9999 against the oracle's bf16
+  output (the pages' own bank check allows nrmse 0.01-0.02, cos > 0.999);
+* invariants: a token alone equals the batch bit for bit; routed ids equal
+  to n_experts never reach the shared expert.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gemm_mxfp4_dequant_amd import inputs
+from tests.helpers import assert_within, bf16_to_f64, dev, host, ulp_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    from gemm_mxfp4_dequant_amd import mxfp4
+    mxfp4.lib()
+    return mxfp4
+
+
+def bank_case(seed, E, H, I, T, K, shared, routing="softmax", lo=110, hi=125):
+    """Inputs with banks of E (+1 shared) experts; bf16 activations."""
+    c = inputs.moe_case(seed, E + int(shared), H, I, T, K, "bf16", routing,
+                        scale_lo=lo, scale_hi=hi)
+    ids = c["ids"].copy()
+    ids[ids >= E] = ids[ids >= E] % E  # routed ids stay below E
+    c["ids"] = ids.astype(np.int32)
+    return c
+
+
+def run(m, d, E, H, I, lim, shared, **kw):
+    return m.moe_experts_mxfp4_v41(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"],
+                                   d["w"], swiglu_limit=lim, has_shared=shared, **kw)
+
+
+def check(m, orc, c, E, H, I, lim, shared, tokens=None):
+    T, K = c["ids"].shape
+    d = {k: dev(v) for k, v in c.items()}
+    ids_a, w_a, Ea = orc.v41_routing(c["ids"], c["w"], E, shared)
+    Ka = ids_a.shape[1]
+    Pa = T * Ka
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    keep = np.zeros(T, bool)
+    keep[tok] = True
+    ids_k = np.where(keep[:, None], ids_a, -1).astype(np.int32)
+
+    # stage isolation: h in slot order of the augmented routing
+    h = torch.empty((Pa, I), dtype=torch.bfloat16, device="cuda")
+    m.moe_experts_mxfp4_v41_stages(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"],
+                                   d["w"], swiglu_limit=lim, has_shared=shared, h_out=h)
+    _, _, slot = m.moe_route_group(dev(ids_a), Ea)
+    slot = host(slot)
+    h_gpu = host(h)
+    st = orc.moe_gate_up(c["gate"], c["up"], Ea, H, I, c["x"], ids_k, False)
+    h_or = orc.moe_v41_act(st["g"], st["u"], w_a, ids_k, Ea, lim)
+    flat = ids_k.reshape(-1)
+    valid = np.where((flat >= 0) & (flat < Ea))[0]
+    hp = bf16_to_f64(h_gpu[slot[valid]])
+    g, u = st["g"][valid], st["u"][valid]
+    gb = bf16_to_f64(orc.bf16_rne_array(g)).reshape(g.shape)
+    ub = bf16_to_f64(orc.bf16_rne_array(u)).reshape(u.shape)
+    if lim > 0:
+        ub = np.clip(ub, -lim, lim)
+        gb = np.minimum(gb, lim)
+    wv = np.abs(w_a.reshape(-1)[valid])[:, None]
+    dg = 1e-4 * st["mag_g"][valid] + ulp_bf16(g)
+    du = 1e-4 * st["mag_u"][valid] + ulp_bf16(u)
+    silu_b = gb / (1.0 + np.exp(-np.clip(gb, -700, 700)))
+    bound = wv * (1.1 * dg * np.abs(ub) + np.abs(silu_b) * du)
+    # the bound is absolute (already holds the 1e-4 product rule)
+    assert_within(hp, h_or[valid], np.zeros_like(bound), extra=bound + ulp_bf16(h_or[valid]),
+                  what="h (V4.1)")
+
+    # down + combine fed with the device h
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    m.moe_experts_mxfp4_v41_stages(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"],
+                                   d["w"], swiglu_limit=lim, has_shared=shared, out=out,
+                                   h_in=dev(h_gpu))
+    out_g = bf16_to_f64(host(out))
+    h_pair = np.zeros((Pa, I))
+    vv = np.where(slot >= 0)[0]
+    h_pair[vv] = bf16_to_f64(h_gpu[slot[vv]])
+    y, mag_y = orc.moe_down(c["down"], Ea, H, I, h_pair, ids_k)
+    o, mag_o = orc.moe_combine(y, mag_y, np.ones(ids_k.shape), ids_k, Ea)
+    assert_within(out_g[tok], o[tok], mag_o[tok], extra=ulp_bf16(o[tok]), what="down+combine")
+
+    # end to end against the oracle's own chain
+    out2 = bf16_to_f64(host(run(m, d, E, H, I, lim, shared)))
+    ref = orc.moe_v41(c["gate"], c["up"], c["down"], E, H, I, c["x"][tok], c["ids"][tok],
+                      c["w"][tok], lim, shared)
+    ref = bf16_to_f64(ref["out_bf16"])
+    got = out2[tok]
+    nrmse = np.sqrt(np.mean((got - ref) ** 2)) / np.sqrt(np.mean(ref ** 2))
+    cos = float((got * ref).sum() / np.sqrt((got * got).sum() * (ref * ref).sum()))
+    assert nrmse < 2e-3 and cos > 0.9999, (nrmse, cos)
+    return out2
+
+
+@pytest.mark.parametrize("lim", [0.0, 1.5])
+@pytest.mark.parametrize("shared", [False, True])
+def test_small_bank(m, orc, lim, shared):
+    """Few tokens per expert (skinny kernels); the limit clamps many values."""
+    E, H, I, T, K = 8, 512, 256, 9, 3
+    check(m, orc, bank_case(80 + int(shared), E, H, I, T, K, shared), E, H, I, lim, shared)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_many_tokens_per_expert(m, orc, shared):
+    """Tens of tokens per expert (tiled kernels), ragged column tiles."""
+    E, H, I, T, K = 4, 1024, 512, 90, 2
+    check(m, orc, bank_case(84, E, H, I, T, K, shared), E, H, I, 2.0, shared)
+
+
+def test_dropped_ids_never_reach_the_shared_expert(m, orc):
+    E, H, I, T, K = 6, 512, 256, 7, 2
+    c = bank_case(86, E, H, I, T, K, True)
+    c["ids"][1, 0] = -1
+    c["ids"][2, 1] = E       # the shared expert's index: must be dropped
+    c["ids"][4, 0] = E + 40
+    check(m, orc, c, E, H, I, 1.0, True)
+
+
+def test_prefill_shape_sampled(m, orc):
+    """The 256-expert prefill layer with a shared expert and limit 10, a few
+    tokens checked (full-size run)."""
+    cfg = inputs.WORKLOADS[5]
+    E, H, I, T, K = (cfg["n_experts"], cfg["hidden"], cfg["inter"], cfg["n_tokens"],
+                     cfg["top_k"])
+    c = inputs.workload_case(5)
+    rng = inputs.rng_for(55)
+    sh = [inputs.draw_weights(rng, I, H, cfg["scale_lo"], cfg["scale_hi"]),
+          inputs.draw_weights(rng, I, H, cfg["scale_lo"], cfg["scale_hi"]),
+          inputs.draw_weights(rng, H, I, cfg["scale_lo"], cfg["scale_hi"])]
+    c = dict(c)
+    for k, s in zip(("gate", "up", "down"), sh):
+        c[k] = np.concatenate([c[k], s])
+    toks = np.random.default_rng(6).choice(T, 3, replace=False)
+    check(m, orc, c, E, H, I, 10.0, True, tokens=toks)
+
+
+def test_token_alone_equals_batch_bitwise(m):
+    E, H, I, T, K = 5, 1024, 512, 80, 2
+    c = bank_case(88, E, H, I, T, K, True)
+    d = {k: dev(v) for k, v in c.items()}
+    ob = host(run(m, d, E, H, I, 3.0, True))
+    for t in (0, 41, 79):
+        dt = dict(d)
+        dt["x"], dt["ids"], dt["w"] = d["x"][t:t + 1], d["ids"][t:t + 1], d["w"][t:t + 1]
+        o1 = host(run(m, dt, E, H, I, 3.0, True))
+        assert np.array_equal(o1[0], ob[t]), t
