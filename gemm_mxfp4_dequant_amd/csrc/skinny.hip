@@ -247,19 +247,36 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
     const uint8_t *A1 = (MODE == MODE_GATEUP) ? a.w1 + (int64_t)tm.expert * a.expert_stride : A0;
     const int64_t code_bytes = (int64_t)R * (C / 2);
 
-    // ---- 1. activation and scale loads, issued before the weight loads so
-    //         that waiting for them does not wait for HBM
+    // ---- 1.-2. activation, scale and weight loads.  The activations and
+    // scales go first so that staging them does not wait for HBM (measured:
+    // starting the weight stream first in the expert gate/up, whose
+    // activation rows sit behind one more dependent load, made the 64-expert
+    // decode layer 6 % slower).
     const int segs = C / 8;
     const int units = tm.ntok * segs;
     float xv[UMAX][8];
+    auto load_acts = [&]() {
 #pragma unroll
-    for (int q = 0; q < UMAX; ++q) {
-        const int u = tid + q * NT;
-        if (u < units) {
-            const int t = u / segs;
-            load_unit<MODE, XBF>(a, tm.slot0, t, u - t * segs, C, xv[q]);
+        for (int q = 0; q < UMAX; ++q) {
+            const int u = tid + q * NT;
+            if (u < units) {
+                const int t = u / segs;
+                load_unit<MODE, XBF>(a, tm.slot0, t, u - t * segs, C, xv[q]);
+            }
         }
-    }
+    };
+    auto arow_of = [&](int row0) {
+        const int r = min(row0 + tile * 16 + li, R - 1);
+        return (mat ? A1 : A0) + (int64_t)r * (C / 2) + wk * (KW / 2) + ls * 16;
+    };
+    u32x4 cw[LS];
+    auto load_codes = [&]() {
+        const uint8_t *arow = arow_of(rb_first * rows_wg);
+#pragma unroll
+        for (int L = 0; L < LS; ++L)
+            cw[L] = *reinterpret_cast<const u32x4 *>(arow + L * 64);
+    };
+    load_acts();
     // scale chunk of this thread: one 16-byte chunk per thread per row block
     // (threads past the chunk count re-read the last chunk and do not store)
     const int sch = gpr / 16;                // 16-byte scale chunks per row
@@ -276,19 +293,7 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
                                                  sc16 * 16);
     };
     u32x4 sv = load_scales(rb_first * rows_wg);
-
-    // ---- 2. this wave's weight loads (first row block)
-    auto arow_of = [&](int row0) {
-        const int r = min(row0 + tile * 16 + li, R - 1);
-        return (mat ? A1 : A0) + (int64_t)r * (C / 2) + wk * (KW / 2) + ls * 16;
-    };
-    u32x4 cw[LS];
-    {
-        const uint8_t *arow = arow_of(rb_first * rows_wg);
-#pragma unroll
-        for (int L = 0; L < LS; ++L)
-            cw[L] = *reinterpret_cast<const u32x4 *>(arow + L * 64);
-    }
+    load_codes();
 
     // ---- 3. activations and scales -> LDS
 #pragma unroll
