@@ -131,6 +131,7 @@ class Timer:
         torch = self.torch
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        self.run(1)  # one warm pass (a replay right after capture runs slower)
         torch.cuda.synchronize()
         e0.record()
         self.run(reps)
