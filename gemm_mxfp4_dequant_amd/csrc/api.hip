@@ -355,13 +355,12 @@ int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_d
     const int64_t tnch = (b + mx::tiled_tokens(xbf, tnc) - 1) / mx::tiled_tokens(xbf, tnc);
     const int rpw = mx::tiled_rows_per_wg(TILED_NW_GEMM, 1);
     const int64_t twgs = tnch * ((rows + rpw - 1) / rpw);
-    if (xbf && b > maxc && mx::tiled_supported((int)cols) && twgs >= TILED_MIN_WGS) {
-        // bf16 tokens beyond one skinny chunk and enough row blocks to fill
-        // the chip: the tiled kernel, one pass over the weights per 64 tokens
-        // (measured, 14336 x 4096: b = 64 in 20.9 us against 40.1 us for four
-        // skinny chunks; with 64 workgroups, 4096 x 4096, it loses 2x).  fp32
-        // tokens stay on the skinny path, which splits them into hi/lo once
-        // per workgroup instead of once per fragment read.
+    if (b > maxc && mx::tiled_supported((int)cols) && twgs >= TILED_MIN_WGS) {
+        // tokens beyond one skinny chunk and enough row blocks to fill the
+        // chip: the tiled kernel, one pass over the weights per 64 bf16 / 32
+        // fp32 tokens (measured, 14336 x 4096: bf16 b = 64 in 20.9 us
+        // against 40.1 us for four skinny chunks; with 64 workgroups,
+        // 4096 x 4096, it loses 2x).
         const int nc = tnc;
         const int64_t nch = tnch;
         if (twgs > ((int64_t)1 << 31) - 1)

@@ -62,23 +62,43 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Exact split of fp32 into bf16 hi + lo for 8 values: hi = RNE(x),
-// lo = RNE(x - hi) (x - hi is exact in fp32); |x - hi - lo| <= 2^-16 |x|.
+// Exact split of fp32 into bf16 hi + lo: hi = RNE(x), lo = RNE(x - hi)
+// (x - hi is exact in fp32); |x - hi - lo| <= 2^-16 |x|.  Two values, packed
+// as one word each (element 0 in the low half).
+__device__ __forceinline__ void split_bf16_pair(float x0, float x1, uint32_t &hi, uint32_t &lo)
+{
+    const f32x2 v = {x0, x1};
+    const bf16x2 h = __builtin_convertvector(v, bf16x2);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    const f32x2 hf = {__uint_as_float(hb << 16), __uint_as_float(hb & 0xFFFF0000u)};
+    const f32x2 r = {v[0] - hf[0], v[1] - hf[1]};
+    hi = hb;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+}
+
+// The split of 8 values (MFMA operands).
 __device__ __forceinline__ void split_bf16x8(const float *x, bf16x8 &hi, bf16x8 &lo)
 {
+    u32x4 h, l;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        f32x2 v = {x[2 * i], x[2 * i + 1]};
-        bf16x2 h = __builtin_convertvector(v, bf16x2);
-        uint32_t hb = __builtin_bit_cast(uint32_t, h);
-        f32x2 hf = {__uint_as_float(hb << 16), __uint_as_float(hb & 0xFFFF0000u)};
-        f32x2 r = {v[0] - hf[0], v[1] - hf[1]};
-        bf16x2 l = __builtin_convertvector(r, bf16x2);
-        hi[2 * i] = h[0];
-        hi[2 * i + 1] = h[1];
-        lo[2 * i] = l[0];
-        lo[2 * i + 1] = l[1];
+        uint32_t hw, lw;
+        split_bf16_pair(x[2 * i], x[2 * i + 1], hw, lw);
+        h[i] = hw;
+        l[i] = lw;
     }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// The split of 4 values (half an MFMA operand).
+__device__ __forceinline__ void split_bf16x4(f32x4 x, u32x2 &hi, u32x2 &lo)
+{
+    uint32_t h0, l0, h1, l1;
+    split_bf16_pair(x[0], x[1], h0, l0);
+    split_bf16_pair(x[2], x[3], h1, l1);
+    hi = u32x2{h0, h1};
+    lo = u32x2{l0, l1};
 }
 
 // Round fp32 to bf16, nearest-even (v_cvt_pk_bf16_f32); inf/NaN kept.

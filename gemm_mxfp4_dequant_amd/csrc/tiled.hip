@@ -25,6 +25,11 @@
 //  * The activation slab is stored XOR-swizzled (16-byte chunk k of token t
 //    at position k ^ (t & 15)), so the 16 lanes reading one MFMA fragment
 //    hit distinct banks.
+//  * fp32 tokens: once a step's slab has landed, the workgroup splits it
+//    into bf16 hi / lo rows (hi of token 8c + i in MFMA column i of tile c,
+//    lo in column 8 + i), once per step rather than once per wave and
+//    fragment, behind one more barrier; the MFMA then reads these rows the
+//    way it reads bf16 tokens.
 //  * Work items come from the same grouping as the skinny kernel
 //    ("rlx-cpu 0.2.17, src/gguf_matmul.rs", grouped_moe_sort_plan): an
 //    expert's rows are streamed once per item of up to 16 * NC tokens
@@ -73,6 +78,13 @@ __device__ __forceinline__ void lds_dma4(const void *g, void *lds)
     __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
 }
 
+// s_waitcnt lgkmcnt(0) with the other counters left alone: this wave's LDS
+// writes are done.
+__device__ __forceinline__ void wait_lgkm0()
+{
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // Workgroup barrier without a memory fence (a fence would wait for every
 // load in flight); the compiler barriers keep LDS accesses on their side.
 __device__ __forceinline__ void raw_barrier()
@@ -106,6 +118,9 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     // scale bytes of one 512-column unit: [NW][64 lanes][16 B], loaded with
     // stage 0 (the unit's first step) and read into registers at that step
     __shared__ __align__(16) uint8_t scs[NW * 1024];
+    // fp32 tokens: the current step's slab as bf16 hi / lo rows, 16 * NC rows
+    // of 128 columns, 16-byte chunk p of row r at position p ^ (r & 15)
+    __shared__ __align__(16) uint8_t cvb[XBF ? 16 : NC * 16 * 256];
     auto stage = [&] __device__(auto tag) -> uint8_t * {
         constexpr int k = decltype(tag)::value;
         if constexpr (k == 0)
@@ -234,6 +249,31 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
                 issue(IntTag<(j + 3) % TNS>{}, min(s + 3, nsteps - 1));
 
                 const uint8_t *S = stage(IntTag<j>{});
+                if constexpr (!XBF) {
+                    // split the slab's first 8 * NCU tokens (token t, chunk k
+                    // of four columns) into rows 16 (t / 8) + t % 8 (hi) and
+                    // + 8 (lo)
+                    constexpr int CCH = NCU * 8 * 32;
+#pragma unroll
+                    for (int i0 = 0; i0 < CCH; i0 += NW * 64) {
+                        const int i = i0 + tid;
+                        if (CCH % (NW * 64) == 0 || i < CCH) {
+                            const int t = i >> 5, k = i & 31;
+                            const f32x4 v = *reinterpret_cast<const f32x4 *>(
+                                S + ACT_OFF + t * ROWB + (k ^ (t & 15)) * 16);
+                            u32x2 hi, lo;
+                            split_bf16x4(v, hi, lo);
+                            const int rh = (t >> 3) * 16 + (t & 7), rl = rh + 8;
+                            const int p = k >> 1, o = (k & 1) * 8;
+                            *reinterpret_cast<u32x2 *>(cvb + rh * 256 + (p ^ (rh & 15)) * 16 + o) =
+                                hi;
+                            *reinterpret_cast<u32x2 *>(cvb + rl * 256 + (p ^ (rl & 15)) * 16 + o) =
+                                lo;
+                        }
+                    }
+                    wait_lgkm0();
+                    raw_barrier();
+                }
                 if constexpr (j == 0) { // this unit's scales, before they are refilled
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
@@ -250,31 +290,16 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
+                    // MFMA column li of tile c: bf16 token 16 c + li, or the
+                    // hi / lo row 16 c + li of the split fp32 slab (256-byte
+                    // rows, swizzled alike)
+                    const uint8_t *B = XBF ? S + ACT_OFF : cvb;
                     bf16x8 bv[NCU];
 #pragma unroll
                     for (int c = 0; c < NCU; ++c) {
-                        if constexpr (XBF) {
-                            const int t = c * 16 + li;
-                            const int p = (4 * ls + m) ^ li;
-                            bv[c] = *reinterpret_cast<const bf16x8 *>(S + ACT_OFF + t * ROWB +
-                                                                      p * 16);
-                        } else {
-                            const int t = c * 8 + (li & 7);
-                            const int k0 = 8 * ls + 2 * m;
-                            const f32x4 v0 = *reinterpret_cast<const f32x4 *>(
-                                S + ACT_OFF + t * ROWB + (k0 ^ (t & 15)) * 16);
-                            const f32x4 v1 = *reinterpret_cast<const f32x4 *>(
-                                S + ACT_OFF + t * ROWB + ((k0 + 1) ^ (t & 15)) * 16);
-                            float v[8];
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                v[i] = v0[i];
-                                v[4 + i] = v1[i];
-                            }
-                            bf16x8 hi, lo;
-                            split_bf16x8(v, hi, lo);
-                            bv[c] = li < 8 ? hi : lo;
-                        }
+                        const int r = c * 16 + li;
+                        const int p = (4 * ls + m) ^ li;
+                        bv[c] = *reinterpret_cast<const bf16x8 *>(B + r * 256 + p * 16);
                     }
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
@@ -373,10 +398,9 @@ struct TEntry {
 // expert bank: gate/up 8 waves x 1 row tile (four 32 KB stages), down 8 x 2
 // (one activation slab serves 256 rows: 1.67 -> 1.59 ms on the prefill bank);
 // GEMM: 4 waves x 1 row tile (more workgroups on 14336-row weights)
-// (GEMMs take this path with bf16 tokens only)
 const TEntry kTiled[] = {
     MX_TX(MODE_GATEUP, 8, 1, 4), MX_TX(MODE_DOWN, 8, 2, 4),
-    MX_T(MODE_GEMM, 1, 4, 1, 4), MX_T(MODE_GEMM, 1, 4, 1, 2),
+    MX_TX(MODE_GEMM, 4, 1, 4), MX_TX(MODE_GEMM, 4, 1, 2),
 };
 
 const TEntry *tfind(int mode, bool xbf, int nw, int rt, int nc)

@@ -97,8 +97,8 @@ def test_wide_scale_range(m, orc):
                                    (40, "bf16"), (64, "bf16")])
 def test_tiled_shapes(m, orc, b, xdt):
     """Enough row blocks for the tiled kernel (12300 rows, a ragged last
-    block), 1 to 4 column tiles in use (bf16 activations; fp32 ones take
-    the skinny path)."""
+    block), 1 to 4 column tiles in use, bf16 activations and fp32 ones
+    (split into hi / lo rows once per K step)."""
     check(m, orc, 12300, 1024, b, 700 + b, xdt=xdt)
 
 
