@@ -354,6 +354,18 @@ def main():
                                    **spread_us(t, 30)}
         log(f"moe_decode_e64: {extra['moe_decode_e64']}")
         del s, t
+        # the device router on the routing sizes of both layers (outside the
+        # layer's own timing: the layer takes its routing as input)
+        for name, (T, E, K) in (("route_topk_8x64_k6", (8, 64, 6)),
+                                ("route_topk_512x256_k8", (512, 256, 8))):
+            L = torch.from_numpy(inputs.gating_logits(inputs.rng_for(T + E), T, E)).cuda()
+            ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+            w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+            t = Timer(torch, [lambda: mx.moe_route_topk(L, K, ids, w)] * 50, args.eager)
+            ms = t.time(20)
+            extra[name] = {"us": round(ms * 1e3, 3)}
+            log(f"{name}: {extra[name]}")
+            del L, ids, w, t
         torch.cuda.empty_cache()
     if "prefill" in sections:
         if True:

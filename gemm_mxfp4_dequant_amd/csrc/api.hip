@@ -432,6 +432,27 @@ int moe_route_group(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k, in
     return launched(mx::group_launch(g, (hipStream_t)stream), "group");
 }
 
+int moe_route_topk(const float *logits, int64_t n_tokens, int64_t n_experts, int64_t top_k,
+                   int32_t *topk_ids, float *topk_w, void *stream)
+{
+    clear_error();
+    if (n_experts < 1 || n_experts > MXFP4_MAX_EXPERTS)
+        return fail(MXFP4_EINVAL, "n_experts = %lld outside [1, %d]", (long long)n_experts,
+                    MXFP4_MAX_EXPERTS);
+    if (top_k < 1 || top_k > MXFP4_MAX_TOP_K || top_k > n_experts)
+        return fail(MXFP4_EINVAL, "top_k = %lld outside [1, min(%d, n_experts)]",
+                    (long long)top_k, MXFP4_MAX_TOP_K);
+    if (n_tokens < 1 || n_tokens > MXFP4_MAX_TOKENS)
+        return fail(MXFP4_EINVAL, "n_tokens = %lld outside [1, %d]", (long long)n_tokens,
+                    MXFP4_MAX_TOKENS);
+    TRY(check_buffer("logits", logits, 4));
+    TRY(check_buffer("topk_ids", topk_ids, 4));
+    TRY(check_buffer("topk_w", topk_w, 4));
+    return launched(mx::route_topk_launch(logits, (int)n_tokens, (int)n_experts, (int)top_k,
+                                          topk_ids, topk_w, (hipStream_t)stream),
+                    "route");
+}
+
 size_t moe_experts_mxfp4_workspace_size(int64_t n_tokens, int64_t top_k, int64_t n_experts,
                                         int64_t hidden, int64_t inter, int x_dtype)
 {

@@ -88,6 +88,11 @@ hipError_t combine_launch(const float *y, const int32_t *slot_of_pair, const flo
                           int n_tokens, int top_k, int hidden, void *out, bool out_bf16,
                           hipStream_t stream);
 
+// Top-k routing of gating logits [n_tokens][n_experts] (n_experts <= 1024,
+// top_k <= 32): ids / w [n_tokens][top_k] in rank order, weights renormalised.
+hipError_t route_topk_launch(const float *logits, int n_tokens, int n_experts, int top_k,
+                             int32_t *ids, float *w, hipStream_t stream);
+
 // Copy h rows (slot order) between a caller buffer and the workspace.
 hipError_t copy_launch(void *dst, const void *src, size_t bytes, hipStream_t stream);
 

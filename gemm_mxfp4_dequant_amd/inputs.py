@@ -80,10 +80,16 @@ def draw_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     return to_bf16_bits(draw_f32(rng, shape))
 
 
+def gating_logits(rng: np.random.Generator, n_tokens: int, n_experts: int) -> np.ndarray:
+    """N(0,1) fp32 gating logits [n_tokens, n_experts]."""
+    return rng.standard_normal((n_tokens, n_experts), dtype=np.float32)
+
+
 def route_softmax(rng: np.random.Generator, n_tokens: int, n_experts: int, top_k: int):
-    """N(0,1) logits, softmax in fp64, top-k by logit (lower index wins a
-    tie), weights renormalised over the chosen k and stored as fp32."""
-    logits = rng.standard_normal((n_tokens, n_experts), dtype=np.float32).astype(np.float64)
+    """The 64-expert decode workload's routing, drawn for its inputs: N(0,1)
+    logits, softmax in fp64, top-k by logit (lower index wins a tie),
+    weights renormalised over the chosen k and stored as fp32."""
+    logits = gating_logits(rng, n_tokens, n_experts).astype(np.float64)
     z = np.exp(logits - logits.max(axis=1, keepdims=True))
     p = z / z.sum(axis=1, keepdims=True)
     order = np.argsort(-logits, axis=1, kind="stable")[:, :top_k]

@@ -48,6 +48,7 @@ def lib() -> ctypes.CDLL:
         "mxfp4_matvec": (I, [P, I64, I64, P, P, P]),
         "mxfp4_gemm": (I, [P, I64, I64, P, I, I64, P, I, P]),
         "moe_route_group": (I, [P, I64, I64, I64, P, P, P, P]),
+        "moe_route_topk": (I, [P, I64, I64, I64, P, P, P]),
         "moe_experts_mxfp4_workspace_size": (ctypes.c_size_t, [I64, I64, I64, I64, I64, I]),
         "moe_experts_mxfp4": (I, [P, P, P, I64, I64, I64, P, I, I64, P, P, I64, P, I, P,
                                   ctypes.c_size_t, P]),
@@ -145,6 +146,19 @@ def moe_route_group(topk_ids, n_experts, offsets=None, pair_of_slot=None, slot_o
     _check(lib().moe_route_group(_ptr(topk_ids), T, K, n_experts, _ptr(offsets),
                                  _ptr(pair_of_slot), _ptr(slot_of_pair), _stream(stream)))
     return offsets, pair_of_slot, slot_of_pair
+
+
+def moe_route_topk(logits, top_k, topk_ids=None, topk_w=None, stream=None):
+    """Top-k experts and renormalised weights of fp32 logits [T, E]."""
+    T, E = logits.shape
+    dev = logits.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    _check(lib().moe_route_topk(_ptr(logits), T, E, top_k, _ptr(topk_ids), _ptr(topk_w),
+                                _stream(stream)))
+    return topk_ids, topk_w
 
 
 def moe_experts_mxfp4_workspace_size(n_tokens, top_k, n_experts, hidden, inter, x_dtype) -> int:

@@ -97,6 +97,27 @@ int moe_route_group(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k, in
                     int32_t *offsets, int32_t *pair_of_slot, int32_t *slot_of_pair,
                     void *stream);
 
+/* Device router: top-k experts of each token from its gating logits, and
+ * renormalised route weights.  The pages give no router (their MoE frame,
+ * "cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs", takes the picks and weights
+ * as inputs); this is the routing the 64-expert decode workload states:
+ * softmax over the logits, the top_k most probable kept, their
+ * probabilities renormalised to sum to 1.
+ *   logits [n_tokens][n_experts] fp32 (device).
+ *   topk_ids [n_tokens][top_k] (device): slot k holds the expert of rank k,
+ *       ranks by descending logit; equal logits rank the lower index first;
+ *       -0 equals +0; NaN ranks below every number.
+ *   topk_w [n_tokens][top_k] fp32 (device): w_k = exp(l_k - l_0) /
+ *       sum_j exp(l_j - l_0) over the chosen logits, l_0 the largest (equal
+ *       to p_k / sum_j p_j of the full softmax); fp32 expf, summed in slot
+ *       order.  Finite logits give finite weights; otherwise IEEE arithmetic
+ *       of this formula (e.g. NaN when the largest is +inf).
+ * 1 <= n_experts <= MXFP4_MAX_EXPERTS, 1 <= top_k <= min(MXFP4_MAX_TOP_K,
+ * n_experts).  Pointers 4-byte aligned (MXFP4_EALIGN).  The output feeds
+ * moe_experts_mxfp4 and moe_route_group directly. */
+int moe_route_topk(const float *logits, int64_t n_tokens, int64_t n_experts, int64_t top_k,
+                   int32_t *topk_ids, float *topk_w, void *stream);
+
 /* Workspace bytes moe_experts_mxfp4 needs for these sizes (0 on bad sizes). */
 size_t moe_experts_mxfp4_workspace_size(int64_t n_tokens, int64_t top_k, int64_t n_experts,
                                         int64_t hidden, int64_t inter, int x_dtype);

@@ -224,6 +224,38 @@ def group(topk_ids, n_experts: int):
     return counts[:n_experts], offsets, pos[:n_valid], slot[:P]
 
 
+def route_topk(logits, top_k: int):
+    """Router: for each token, the softmax of its gating logits (fp64), the
+    top_k experts by logit, and their probabilities renormalised to sum to 1.
+
+    The pages give no router (their MoE frame takes picks and weights as
+    inputs); this is the routing stated for the 64-expert decode workload
+    (softmax over the logits, top 6, renormalised), with these readings:
+    larger logit first, equal logits lower index first, -0 equal to +0, and
+    NaN ranked below every number and given probability 0.  Returns
+    (ids int32 [T, K], w fp64 [T, K]).  Pinned by test_oracle_router
+    (exhaustive rank order on small rows, two-expert closed form, shift
+    invariance, uniform rows)."""
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    ids = np.empty((T, top_k), np.int32)
+    w = np.empty((T, top_k), np.float64)
+    for t in range(T):
+        row = L[t]
+        nan = np.isnan(row)
+        # rank: numbers by descending value (+0 and -0 compare equal), then
+        # NaN; the expert index breaks ties
+        order = sorted(range(E), key=lambda e: (bool(nan[e]), 0.0 if nan[e] else -row[e], e))
+        chosen = order[:top_k]
+        v = np.where(nan, -np.inf, row)
+        z = np.exp(v - v.max())
+        p = z / z.sum()
+        sel = p[chosen]
+        ids[t] = chosen
+        w[t] = sel / sel.sum()
+    return ids, w
+
+
 def _sanitize_ids(topk_ids, n_experts):
     ids = np.ascontiguousarray(topk_ids, dtype=np.int32).copy()
     ids[(ids < 0) | (ids >= n_experts)] = -1

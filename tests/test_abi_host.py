@@ -36,7 +36,7 @@ def m():
 
 def test_exports_every_declared_symbol(m):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     L = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(L, n), n
@@ -142,6 +142,25 @@ def test_v41_refusals(m):
     r = L.moe_experts_mxfp4_v41_stages(FAKE, FAKE, FAKE, 256, 1024, 512, FAKE, 16, FAKE, FAKE, 8,
                                        10.0, 1, None, FAKE, ws1, None, None, None)
     assert r == m.MXFP4_EINVAL                          # nothing requested
+
+
+def test_router_refusals(m):
+    """The router refuses top_k above n_experts or 32, n_experts outside
+    [1, 1024], no tokens, and unaligned pointers, before any launch."""
+    L = m.lib()
+
+    def call(T=8, E=64, K=6, logits=FAKE, ids=FAKE, w=FAKE):
+        return L.moe_route_topk(logits, T, E, K, ids, w, None)
+
+    assert call(K=65) == m.MXFP4_EINVAL
+    assert "top_k" in m.mxfp4_last_error()
+    assert call(K=33, E=64) == m.MXFP4_EINVAL
+    assert call(K=0) == m.MXFP4_EINVAL
+    assert call(E=1025, K=8) == m.MXFP4_EINVAL
+    assert call(E=0, K=1) == m.MXFP4_EINVAL
+    assert call(T=0) == m.MXFP4_EINVAL
+    assert call(logits=None) == m.MXFP4_EINVAL
+    assert call(ids=FAKE + 2) == m.MXFP4_EALIGN
 
 
 def test_stage_refusals(m):
