@@ -17,8 +17,9 @@
  *
  * Conventions for every entry point:
  *   - Pointers named w, gate, up, down, x, y, out, workspace are DEVICE
- *     pointers owned by the caller and must be 16-byte aligned; topk_ids
- *     and topk_w are device pointers, 4-byte aligned.
+ *     pointers owned by the caller and must be 16-byte aligned; logits,
+ *     topk_ids, topk_w and the grouping arrays are device pointers, 4-byte
+ *     aligned.
  *   - stream is a hipStream_t (NULL = the default stream).  Calls enqueue
  *     kernels on it and return: no host synchronisation, no allocation, no
  *     pointer kept after return.
