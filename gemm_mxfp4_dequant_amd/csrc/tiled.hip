@@ -139,17 +139,32 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     const int nsteps = C / TKS; // a multiple of 4 (cols % 512 == 0)
     const int nunits = nsteps / 4;
 
-    // ---- work item (XCD-grouped logical id, item fastest)
-    const int lid = xcd_logical(blockIdx.x, gridDim.x);
-    const int sub = lid % a.nch;
-    const int row0 = (lid / a.nch) * RB;
+    // ---- work item (XCD-grouped logical id).  GEMM: token chunks fastest,
+    // so the chunks of a row block share its weights in one XCD's L2.
+    // Expert bank: row blocks fastest over the n_work real items only (the
+    // grid is sized by an upper bound; the surplus workgroups, dispatched
+    // last, exit), so an item's gathered activation rows stay in one XCD's
+    // L2 across its row blocks and the items of a hot expert run side by
+    // side on one XCD.
+    int sub, row0;
+    if (MODE == MODE_GEMM) {
+        const int lid = xcd_logical(blockIdx.x, gridDim.x);
+        sub = lid % a.nch;
+        row0 = (lid / a.nch) * RB;
+    } else {
+        const int nrb = (R + RB - 1) / RB;
+        const int real = *a.n_work * nrb;
+        if ((int)blockIdx.x >= real)
+            return;
+        const int lid = xcd_logical(blockIdx.x, real);
+        sub = lid / nrb;
+        row0 = (lid % nrb) * RB;
+    }
     int ntok, slot0, expert = 0;
     if (MODE == MODE_GEMM) {
         slot0 = sub * TPD;
         ntok = min(TPD, a.b - slot0);
     } else {
-        if (sub >= *a.n_work)
-            return;
         const int4 wk = reinterpret_cast<const int4 *>(a.work)[sub];
         expert = wk.x;
         slot0 = wk.y;
