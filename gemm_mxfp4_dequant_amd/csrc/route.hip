@@ -172,8 +172,8 @@ __global__ __launch_bounds__(GT) void group_kernel(GroupArgs g, int nch)
 // offsets, gives each pair its slot; the scatter is then one store per
 // pair.  Same result as the chunked kernel: pairs sorted by (expert, index).
 constexpr int TPW = 8;     // tiles per wave
-constexpr int KEYBITS = 11; // keys 0..1024: expert ids (at most 1024 experts), and
-                            // 1024 for "no expert"
+constexpr int KEYBITS = 11;     // keys: expert ids 0..1023, and NO_EXPERT
+constexpr int NO_EXPERT = 2047; // key of a dropped pair (above every expert id)
 
 __global__ __launch_bounds__(GT) void group_tiles_kernel(GroupArgs g, int ntiles)
 {
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(GT) void group_tiles_kernel(GroupArgs g, int ntiles
             if (e < 0 || e >= E)
                 e = -1;
         }
-        const int key = e >= 0 ? e : 1024;
+        const int key = e >= 0 ? e : NO_EXPERT;
         uint64_t peers = ~0ull;
 #pragma unroll
         for (int b = 0; b < KEYBITS; ++b) {
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(64) void group_small_kernel(GroupArgs g, int ntiles
             if (e < 0 || e >= E)
                 e = -1;
         }
-        const int key = e >= 0 ? e : 1024;
+        const int key = e >= 0 ? e : NO_EXPERT;
         uint64_t peers = ~0ull;
 #pragma unroll
         for (int b = 0; b < KEYBITS; ++b) {

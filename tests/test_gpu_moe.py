@@ -118,8 +118,11 @@ def check_case(m, orc, c, E, H, I, xbf, sample_pairs=None, e2e=True):
 @pytest.mark.parametrize("xd", ["f32", "bf16"])
 @pytest.mark.parametrize("E,H,I,T,K", [(5, 64, 96, 4, 2), (8, 512, 256, 9, 3), (16, 1024, 512, 20, 4),
                                        (3, 96, 160, 1, 3), (33, 2048, 1024, 6, 6),
-                                       (4, 512, 1024, 40, 2), (6, 1024, 512, 90, 3)])
+                                       (4, 512, 1024, 40, 2), (6, 1024, 512, 90, 3),
+                                       (40, 512, 512, 16, 4), (40, 512, 512, 13, 5)])
 def test_small_banks(m, orc, xd, E, H, I, T, K):
+    # (40, 512, 512, 16, 4) / (40, 512, 512, 13, 5): 64 / 65 pairs, one and
+    # two 64-pair tiles of the grouping
     c = inputs.moe_case(E * 100 + T, E, H, I, T, K, xd, "softmax", scale_lo=100, scale_hi=114)
     check_case(m, orc, c, E, H, I, xd == "bf16")
 
@@ -200,14 +203,16 @@ def test_group_large(m, orc):
 
 
 @pytest.mark.parametrize("xd", ["f32", "bf16"])
-def test_token_alone_equals_batch_bitwise(m, xd):
+@pytest.mark.parametrize("E,H,I,T,K", [(6, 1024, 512, 96, 2), (64, 512, 256, 20, 4)])
+def test_token_alone_equals_batch_bitwise(m, xd, E, H, I, T, K):
     """A token's output is the same bits whether the bank runs it in a batch
-    of 96 (work items of 8 tokens) or alone: one summation order."""
-    E, H, I, T, K = 6, 1024, 512, 96, 2
+    or alone: one summation order.  Batches: 96 tokens on 6 experts (tiled
+    kernels, items of many tokens) and 20 tokens on 64 experts (80 pairs,
+    skinny kernels, items of two tokens)."""
     c = inputs.moe_case(46, E, H, I, T, K, xd, "softmax", scale_lo=100, scale_hi=114)
     d = upload(c)
     ob = host(m.moe_experts_mxfp4(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"], d["w"]))
-    for t in (0, 17, 95):
+    for t in (0, 17, T - 1):
         o1 = host(m.moe_experts_mxfp4(d["gate"], d["up"], d["down"], E, H, I, d["x"][t:t + 1],
                                       d["ids"][t:t + 1], d["w"][t:t + 1]))
         assert np.array_equal(o1[0], ob[t]), t

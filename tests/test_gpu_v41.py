@@ -137,6 +137,18 @@ def test_dropped_ids_never_reach_the_shared_expert(m, orc):
     check(m, orc, c, E, H, I, 1.0, True)
 
 
+@pytest.mark.parametrize("T", [8, 20])
+def test_max_experts_shared_with_dropped_ids(m, orc, T):
+    """The largest bank the entry point takes (1023 routed experts and the
+    shared one, expert id 1023) with dropped pairs, 40 and 100 pairs."""
+    E, H, I, K = 1023, 64, 32, 4
+    c = bank_case(90 + T, E, H, I, T, K, True)
+    c["ids"][0, 0] = -1
+    c["ids"][1, 2] = E
+    c["ids"][T - 1, 1] = -7
+    check(m, orc, c, E, H, I, 1.0, True)
+
+
 def test_prefill_shape_sampled(m, orc):
     """The 256-expert prefill layer with a shared expert and limit 10, a few
     tokens checked (full-size run)."""
