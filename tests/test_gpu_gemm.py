@@ -108,6 +108,14 @@ def test_many_row_blocks_per_workgroup(m, orc):
     check(m, orc, 65553, 512, 40, 31)
 
 
+@pytest.mark.parametrize("b", [1, 3])
+def test_row_walk_odd_block_count(m, orc, b):
+    """65552 rows = 4097 blocks of 16, walked two per workgroup: the last
+    workgroup has a single block (the walk's prefetch and double-buffered
+    reduction end early)."""
+    check(m, orc, 65552, 512, b, 60 + b)
+
+
 @pytest.mark.parametrize("rows,cols", [(300, 2304), (5, 5120), (128, 4096), (64, 7168),
                                        (14336, 4096), (200, 1024), (65553, 512)])
 def test_batch_equals_matvec_bitwise(m, rows, cols):

@@ -150,6 +150,17 @@ def test_zipf_many_tokens(m, orc):
     assert rng is not None
 
 
+def test_row_walk_partial_last_workgroup(m, orc):
+    """Gate/up rows 2080 = 130 blocks of 16, walked four per workgroup (64
+    pairs on 64 experts, items of two tokens, the decode layer's kernel):
+    each item's last workgroup walks two blocks, and the double-buffered
+    reduction alternates within a workgroup; the down product takes 2080
+    columns (the generic kernel)."""
+    E, H, I, T, K = 64, 4096, 2080, 8, 8
+    c = inputs.moe_case(47, E, H, I, T, K, "f32", "softmax", scale_lo=100, scale_hi=114)
+    check_case(m, orc, c, E, H, I, False)
+
+
 def test_workload4_decode_full(m, orc):
     c = inputs.workload_case(4)
     cfg = inputs.WORKLOADS[4]
