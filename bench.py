@@ -240,7 +240,7 @@ def main():
     sections = set(args.sections.split(",")) if not args.quick else set()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no "
               "multi-GPU path.  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
