@@ -92,6 +92,7 @@ constexpr int TILED_NW_GEMM = 4;
 constexpr int TILED_NC = 4;
 constexpr int TILED_MIN_TOKENS = 8;
 constexpr int TILED_MIN_WGS = 192; // GEMM: tiled only with ~one workgroup per CU
+constexpr int TILED_FILL_WGS = 256; // GEMM: one workgroup per CU of MI355X
 
 // Workspace layout of the expert bank.
 struct MoeLayout {
@@ -351,10 +352,23 @@ int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_d
     TRY(check_buffer("y", y, 16));
     const bool xbf = x_dtype == MXFP4_BF16;
     const int maxc = xbf ? 16 : 8;
-    const int tnc = b <= mx::tiled_tokens(xbf, 2) ? 2 : TILED_NC;
-    const int64_t tnch = (b + mx::tiled_tokens(xbf, tnc) - 1) / mx::tiled_tokens(xbf, tnc);
+    // Tiled chunks: two MFMA column tiles (32 bf16 / 16 fp32 tokens) when b
+    // fits in them, else four; fp32 tokens also take two when chunks of
+    // four would not give each CU a workgroup (measured, 14336 x 4096 fp32
+    // b = 32: 224 workgroups of four tiles 26.6 us, 448 of two tiles
+    // 24.6 us, the second chunk re-reading the weights from L2; bf16 b = 64
+    // is slower with two tiles, 23.1 vs 19.4 us, and fp32 b = 16 with
+    // one-tile chunks, 18.5 vs 17.8 us).
     const int rpw = mx::tiled_rows_per_wg(TILED_NW_GEMM, 1);
-    const int64_t twgs = tnch * ((rows + rpw - 1) / rpw);
+    const int64_t trb = (rows + rpw - 1) / rpw;
+    auto chunks = [&](int nc) {
+        return (b + mx::tiled_tokens(xbf, nc) - 1) / mx::tiled_tokens(xbf, nc);
+    };
+    int tnc = b <= mx::tiled_tokens(xbf, 2) ? 2 : TILED_NC;
+    if (!xbf && tnc == TILED_NC && chunks(TILED_NC) * trb < TILED_FILL_WGS)
+        tnc = 2;
+    const int64_t tnch = chunks(tnc);
+    const int64_t twgs = tnch * trb;
     if (b > maxc && mx::tiled_supported((int)cols) && twgs >= TILED_MIN_WGS) {
         // tokens beyond one skinny chunk and enough row blocks to fill the
         // chip: the tiled kernel, one pass over the weights per 64 bf16 / 32
