@@ -10,6 +10,8 @@ the other parity tests: |y - y_oracle| <= 1e-4 sum|w x| + 1e-30 (plus one
 bf16 ulp when y is bf16); the expert bank's stage checks and end-to-end
 nrmse < 1e-3, cos > 0.9999.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -83,3 +85,59 @@ def test_moe_random_banks(m, orc, E, H, I, T, K, xdt, routing, seed):
     from tests.test_gpu_moe import check_case
     c = inputs.moe_case(seed, E, H, I, T, K, xdt, routing, scale_lo=100, scale_hi=114)
     check_case(m, orc, c, E, H, I, xdt == "bf16")
+
+
+WIDE = os.environ.get("MXFP4_WIDE_SWEEP") == "1"
+
+
+@pytest.mark.skipif(not WIDE, reason="wide sweep: set MXFP4_WIDE_SWEEP=1 (about 2 minutes per seed)")
+@pytest.mark.parametrize("seed", [11, 23])
+def test_wide_random_sweep(m, orc, seed):
+    """150 random GEMMs (up to 70000 rows, so that workgroups walk several
+    row blocks; fp32/bf16 in and out; 1-64 tokens) and 40 random expert
+    banks (up to 130 experts, decode-sized banks with 4096 hidden columns
+    among them); every failure is collected before the assert."""
+    from tests.test_gpu_moe import check_case
+    rng = np.random.default_rng(seed)
+    fails = []
+    cols_choices = [32, 64, 96, 480, 512, 544, 1024, 1504, 2048, 2080, 3072, 4096, 5120, 7168,
+                    8192, 16384]
+    for i in range(150):
+        cols = int(rng.choice(cols_choices))
+        r = rng.random()
+        if r < 0.15:
+            rows, cols = int(rng.integers(33000, 70000)), min(cols, 1024)
+        elif r < 0.35:
+            rows, cols = int(rng.integers(10000, 15000)), min(cols, 4096)
+        else:
+            rows = int(rng.integers(1, 5000))
+        if cols >= 8192:
+            rows = min(rows, 1500)
+        b = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 17, 23, 24, 31, 32, 33, 40, 48, 64]))
+        xdt = "bf16" if rng.random() < 0.4 else "f32"
+        ydt = "bf16" if rng.random() < 0.25 else "f32"
+        try:
+            test_gemm_random_shapes(m, orc, rows, cols, b, xdt, ydt, 70000 + i)
+        except AssertionError as e:
+            fails.append(("gemm", rows, cols, b, xdt, ydt, str(e)[:200]))
+    for i in range(40):
+        if i % 5 == 0:
+            E, H = int(rng.choice([32, 64])), 4096
+            I, T, K = int(rng.choice([2048, 2080, 1024])), int(rng.integers(4, 12)), int(
+                rng.integers(4, 9))
+        else:
+            E = int(rng.integers(1, 130))
+            H = int(rng.choice([64, 512, 1024, 1536, 2048, 4096]))
+            I = int(rng.choice([32, 256, 512, 1024, 2048]))
+            T = int(rng.integers(1, 200))
+            K = int(rng.integers(1, min(E, 8) + 1))
+            if H * I > 2048 * 2048 and E > 32:
+                E = 32
+        xdt = "bf16" if rng.random() < 0.5 else "f32"
+        routing = "zipf" if rng.random() < 0.3 else "softmax"
+        c = inputs.moe_case(80000 + i, E, H, I, T, K, xdt, routing, scale_lo=100, scale_hi=114)
+        try:
+            check_case(m, orc, c, E, H, I, xdt == "bf16")
+        except AssertionError as e:
+            fails.append(("moe", E, H, I, T, K, xdt, routing, str(e)[:200]))
+    assert not fails, fails
