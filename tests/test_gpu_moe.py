@@ -151,7 +151,7 @@ def test_zipf_many_tokens(m, orc):
 
 
 def test_row_walk_partial_last_workgroup(m, orc):
-    """Gate/up rows 2080 = 130 blocks of 16, walked four per workgroup (64
+    """Gate/up rows 2080 = 130 blocks of 16, walked eight per workgroup (64
     pairs on 64 experts, items of two tokens, the decode layer's kernel):
     each item's last workgroup walks two blocks, and the double-buffered
     reduction alternates within a workgroup; the down product takes 2080
