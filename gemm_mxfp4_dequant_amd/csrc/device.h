@@ -62,17 +62,21 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Exact split of fp32 into bf16 hi + lo: hi = RNE(x), lo = RNE(x - hi)
-// (x - hi is exact in fp32); |x - hi - lo| <= 2^-16 |x|.  Two values, packed
-// as one word each (element 0 in the low half).
+// Exact-enough split of fp32 into bf16 hi + lo: hi = x truncated to bf16
+// (its top 16 bits, one v_perm for two values), lo = RNE(x - hi), where
+// x - hi is exact in fp32 and |x - hi| < 2^-7 |x|, so
+// |x - hi - lo| <= 2^-8 |x - hi| < 2^-15 |x|.  Truncation keeps hi finite
+// for every finite x (nearest-even would round |x| beyond the bf16 maximum
+// to infinity), at the cost of the nearest-even split's 2^-16 bound.  NaN
+// gives NaN parts; x = +-inf gives hi = x and lo = NaN (inf - inf), so an
+// infinite activation makes every output of its token NaN.  Two values,
+// packed as one word each (element 0 in the low half).
 __device__ __forceinline__ void split_bf16_pair(float x0, float x1, uint32_t &hi, uint32_t &lo)
 {
-    const f32x2 v = {x0, x1};
-    const bf16x2 h = __builtin_convertvector(v, bf16x2);
-    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-    const f32x2 hf = {__uint_as_float(hb << 16), __uint_as_float(hb & 0xFFFF0000u)};
-    const f32x2 r = {v[0] - hf[0], v[1] - hf[1]};
-    hi = hb;
+    const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
+    hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u); // bytes 2,3 of b0, then of b1
+    const f32x2 r = {x0 - __uint_as_float(b0 & 0xFFFF0000u),
+                     x1 - __uint_as_float(b1 & 0xFFFF0000u)};
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
 }
 

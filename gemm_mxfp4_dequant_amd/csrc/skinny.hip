@@ -19,8 +19,8 @@
 //    coalesced 16-byte loads, once per workgroup (expert bank), or loaded
 //    by each lane with its codes (plain GEMM).
 //  * The activations of the (up to TPC) tokens are staged in LDS once per
-//    workgroup as bf16 MFMA operands.  fp32 activations are split exactly
-//    into hi = bf16(x) and lo = bf16(x - hi) (|x - hi - lo| <= 2^-16 |x|)
+//    workgroup as bf16 MFMA operands.  fp32 activations are split into
+//    hi = x truncated to bf16 and lo = bf16(x - hi) (|x - hi - lo| < 2^-15 |x|)
 //    and occupy two MFMA columns each; bf16 activations occupy one.
 //  * Each group is decoded once per workgroup by v_cvt_scalef32_pk_bf16_fp4
 //    straight into the MFMA A operand (exact: E2M1 times a power of two is a

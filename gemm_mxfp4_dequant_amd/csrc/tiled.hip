@@ -259,7 +259,11 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
                 // (step s - 1) is free.  Loads issued after stage j's: two
                 // steps' worth, plus the scale load of the stage-0 step when
                 // that is one of them (j = 2, 3).
+                // (this wave's LDS reads of the previous step, which was
+                // stage j - 1, the one refilled below, are done before the
+                // barrier: the barrier itself orders no memory)
                 wait_vmcnt<(TNS - 2) * GN + (j >= 2 ? 1 : 0)>();
+                wait_lgkm0();
                 raw_barrier();
                 issue(IntTag<(j + 3) % TNS>{}, min(s + 3, nsteps - 1));
 

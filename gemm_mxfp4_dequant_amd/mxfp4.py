@@ -6,6 +6,12 @@ the same name, and raises ``Mxfp4Error`` on a nonzero status.  Every step of
 the computation runs in the library's HIP kernels; if the library is not
 built, every call raises (there is no fallback).  Output tensors may be
 given by the caller or are allocated here with torch.
+
+Before anything reaches the library, every tensor argument is checked here:
+a device tensor on the current device, contiguous, of an accepted element
+type, and at least as long as the sizes passed with it imply.  The C ABI
+cannot see buffer lengths or memory kinds, so a host tensor or a short
+buffer would otherwise reach a kernel.
 """
 from __future__ import annotations
 
@@ -61,6 +67,7 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_float, I, P, P, ctypes.c_size_t, P, P,
                                              P]),
         "mxfp4_last_error": (ctypes.c_char_p, []),
+        "mxfp4_probe_read": (I, [P, I64, I, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -75,12 +82,65 @@ def _check(status: int):
         raise Mxfp4Error(status, lib().mxfp4_last_error().decode())
 
 
+# ---------------------------------------------------------------------------
+# Argument checks.  The C ABI sees raw pointers and sizes only, so this layer
+# is the one place that can refuse a host tensor, a strided view, a wrong
+# element type or a buffer shorter than the sizes claim, before a kernel
+# would read or write outside it.
+# ---------------------------------------------------------------------------
+
+def _req(t, name, dtypes, numel=None, device=None):
+    """Check one tensor argument; returns its device."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device (cuda) tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, other operands on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.dtype not in dtypes:
+        names = ", ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise TypeError(f"{name}: dtype {str(t.dtype).replace('torch.', '')}, expected {names}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, needs at least {numel}")
+    return t.device
+
+
+def _req_shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _req_current(device):
+    """Kernels are launched on the current device's stream: the operands must
+    live there."""
+    cur = torch.cuda.current_device()
+    if device.index is not None and device.index != cur:
+        raise ValueError(f"operands on {device}, current device is cuda:{cur}")
+
+
+_ACT = (torch.float32, torch.bfloat16)
+_U8 = (torch.uint8,)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+
+
+def _sizes(**kw):
+    for k, v in kw.items():
+        if not isinstance(v, int) or isinstance(v, bool):
+            raise TypeError(f"{k}: expected an int, got {type(v).__name__}")
+
+
+def _tensor_bytes(rows, cols):
+    n = mxfp4_nbytes(rows, cols)
+    if n < 0:
+        raise ValueError(f"rows = {rows}, cols = {cols}: not an MXFP4 shape (cols % 32 != 0)")
+    return n
+
+
 def _ptr(t):
-    if t is None:
-        return None
-    if isinstance(t, int):
-        return t
-    return t.data_ptr()
+    return None if t is None else t.data_ptr()
 
 
 def _stream(stream):
@@ -110,39 +170,69 @@ def mxfp4_last_error() -> str:
 
 
 def mxfp4_dequant(w, rows, cols, out=None, out_dtype=torch.float32, stream=None):
+    _sizes(rows=rows, cols=cols)
+    d = _req(w, "w", _U8, _tensor_bytes(rows, cols))
+    _req_current(d)
     if out is None:
         out = torch.empty((rows, cols), dtype=out_dtype, device=w.device)
+    _req(out, "out", _ACT, rows * cols, d)
     _check(lib().mxfp4_dequant(_ptr(w), rows, cols, _ptr(out), _dt(out), _stream(stream)))
     return out
 
 
 def mxfp4_matvec(w, rows, cols, x, y=None, stream=None):
+    _sizes(rows=rows, cols=cols)
+    d = _req(w, "w", _U8, _tensor_bytes(rows, cols))
+    _req_current(d)
+    _req(x, "x", _F32, cols, d)
     if y is None:
         y = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _req(y, "y", _F32, rows, d)
     _check(lib().mxfp4_matvec(_ptr(w), rows, cols, _ptr(x), _ptr(y), _stream(stream)))
     return y
 
 
 def mxfp4_gemm(w, rows, cols, x, b=None, y=None, y_dtype=torch.float32, stream=None):
     if b is None:
-        b = x.shape[0]
+        b = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() >= 1 else 0
+    _sizes(rows=rows, cols=cols, b=b)
+    d = _req(w, "w", _U8, _tensor_bytes(rows, cols))
+    _req_current(d)
+    _req(x, "x", _ACT, b * cols, d)
     if y is None:
         y = torch.empty((b, rows), dtype=y_dtype, device=x.device)
+    _req(y, "y", _ACT, b * rows, d)
     _check(lib().mxfp4_gemm(_ptr(w), rows, cols, _ptr(x), _dt(x), b, _ptr(y), _dt(y),
                             _stream(stream)))
     return y
 
 
+def _routing(topk_ids, d=None, topk_w=None):
+    """Check the routing pair; returns (T, K, device)."""
+    if not isinstance(topk_ids, torch.Tensor) or topk_ids.dim() != 2:
+        raise ValueError("topk_ids: expected a [n_tokens, top_k] tensor")
+    d = _req(topk_ids, "topk_ids", _I32, None, d)
+    if topk_w is not None:
+        _req(topk_w, "topk_w", _F32, None, d)
+        _req_shape(topk_w, "topk_w", topk_ids.shape)
+    T, K = topk_ids.shape
+    return T, K, d
+
+
 def moe_route_group(topk_ids, n_experts, offsets=None, pair_of_slot=None, slot_of_pair=None,
                     stream=None):
-    T, K = topk_ids.shape
-    dev = topk_ids.device
+    _sizes(n_experts=n_experts)
+    T, K, d = _routing(topk_ids)
+    _req_current(d)
     if offsets is None:
-        offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+        offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=d)
     if pair_of_slot is None:
-        pair_of_slot = torch.full((T * K,), -1, dtype=torch.int32, device=dev)
+        pair_of_slot = torch.full((T * K,), -1, dtype=torch.int32, device=d)
     if slot_of_pair is None:
-        slot_of_pair = torch.empty(T * K, dtype=torch.int32, device=dev)
+        slot_of_pair = torch.empty(T * K, dtype=torch.int32, device=d)
+    _req(offsets, "offsets", _I32, n_experts + 1, d)
+    _req(pair_of_slot, "pair_of_slot", _I32, T * K, d)
+    _req(slot_of_pair, "slot_of_pair", _I32, T * K, d)
     _check(lib().moe_route_group(_ptr(topk_ids), T, K, n_experts, _ptr(offsets),
                                  _ptr(pair_of_slot), _ptr(slot_of_pair), _stream(stream)))
     return offsets, pair_of_slot, slot_of_pair
@@ -150,12 +240,18 @@ def moe_route_group(topk_ids, n_experts, offsets=None, pair_of_slot=None, slot_o
 
 def moe_route_topk(logits, top_k, topk_ids=None, topk_w=None, stream=None):
     """Top-k experts and renormalised weights of fp32 logits [T, E]."""
+    _sizes(top_k=top_k)
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise ValueError("logits: expected a [n_tokens, n_experts] tensor")
+    d = _req(logits, "logits", _F32)
+    _req_current(d)
     T, E = logits.shape
-    dev = logits.device
     if topk_ids is None:
-        topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+        topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=d)
     if topk_w is None:
-        topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+        topk_w = torch.empty((T, top_k), dtype=torch.float32, device=d)
+    _req(topk_ids, "topk_ids", _I32, T * top_k, d)
+    _req(topk_w, "topk_w", _F32, T * top_k, d)
     _check(lib().moe_route_topk(_ptr(logits), T, E, top_k, _ptr(topk_ids), _ptr(topk_w),
                                 _stream(stream)))
     return topk_ids, topk_w
@@ -168,19 +264,45 @@ def moe_experts_mxfp4_workspace_size(n_tokens, top_k, n_experts, hidden, inter, 
                                                       inter, code))
 
 
-def _moe_ws(workspace, T, K, E, H, I, x, dev):
-    need = moe_experts_mxfp4_workspace_size(T, K, E, H, I, _dt(x))
+def _bank(gate, up, down, n_tensors, hidden, inter):
+    """Check the three expert banks (n_tensors tensors per role); returns the
+    device."""
+    _sizes(hidden=hidden, inter=inter)
+    tb = _tensor_bytes(inter, hidden)
+    d = _req(gate, "gate", _U8, n_tensors * tb)
+    _req(up, "up", _U8, n_tensors * tb, d)
+    _req(down, "down", _U8, n_tensors * _tensor_bytes(hidden, inter), d)
+    _req_current(d)
+    return d
+
+
+def _ws(workspace, need, d):
+    if need <= 0:
+        raise ValueError("expert bank sizes out of range (workspace size query returned 0)")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    return workspace, workspace.numel() * workspace.element_size()
+        workspace = torch.empty(need, dtype=torch.uint8, device=d)
+    _req(workspace, "workspace", _U8, need, d)
+    return workspace, workspace.numel()
+
+
+def _h_buffers(h_in, h_out, n_slots, inter, dtypes, d):
+    if h_in is not None:
+        _req(h_in, "h_in", dtypes, n_slots * inter, d)
+    if h_out is not None:
+        _req(h_out, "h_out", dtypes, n_slots * inter, d)
 
 
 def moe_experts_mxfp4(gate, up, down, n_experts, hidden, inter, x, topk_ids, topk_w, out=None,
                       out_dtype=torch.bfloat16, workspace=None, stream=None):
-    T, K = topk_ids.shape
+    _sizes(n_experts=n_experts)
+    d = _bank(gate, up, down, n_experts, hidden, inter)
+    T, K, _ = _routing(topk_ids, d, topk_w)
+    _req(x, "x", _ACT, T * hidden, d)
     if out is None:
-        out = torch.empty((T, hidden), dtype=out_dtype, device=x.device)
-    ws, ws_bytes = _moe_ws(workspace, T, K, n_experts, hidden, inter, x, x.device)
+        out = torch.empty((T, hidden), dtype=out_dtype, device=d)
+    _req(out, "out", _ACT, T * hidden, d)
+    ws, ws_bytes = _ws(workspace, moe_experts_mxfp4_workspace_size(T, K, n_experts, hidden,
+                                                                   inter, _dt(x)), d)
     _check(lib().moe_experts_mxfp4(_ptr(gate), _ptr(up), _ptr(down), n_experts, hidden, inter,
                                    _ptr(x), _dt(x), T, _ptr(topk_ids), _ptr(topk_w), K, _ptr(out),
                                    _dt(out), _ptr(ws), ws_bytes, _stream(stream)))
@@ -190,8 +312,15 @@ def moe_experts_mxfp4(gate, up, down, n_experts, hidden, inter, x, topk_ids, top
 def moe_experts_mxfp4_stages(gate, up, down, n_experts, hidden, inter, x, topk_ids, topk_w,
                              out=None, out_dtype=torch.bfloat16, workspace=None, h_in=None,
                              h_out=None, stream=None):
-    T, K = topk_ids.shape
-    ws, ws_bytes = _moe_ws(workspace, T, K, n_experts, hidden, inter, x, x.device)
+    _sizes(n_experts=n_experts)
+    d = _bank(gate, up, down, n_experts, hidden, inter)
+    T, K, _ = _routing(topk_ids, d, topk_w)
+    _req(x, "x", _ACT, T * hidden, d)
+    if out is not None:
+        _req(out, "out", _ACT, T * hidden, d)
+    _h_buffers(h_in, h_out, T * K, inter, (x.dtype,), d)
+    ws, ws_bytes = _ws(workspace, moe_experts_mxfp4_workspace_size(T, K, n_experts, hidden,
+                                                                   inter, _dt(x)), d)
     out_code = _dt(out) if out is not None else (MXFP4_BF16 if out_dtype == torch.bfloat16
                                                  else MXFP4_F32)
     _check(lib().moe_experts_mxfp4_stages(_ptr(gate), _ptr(up), _ptr(down), n_experts, hidden,
@@ -207,11 +336,7 @@ def moe_experts_mxfp4_v41_workspace_size(n_tokens, top_k, n_experts, hidden, int
                                                           inter, int(has_shared)))
 
 
-def _v41_ws(workspace, T, K, E, H, I, has_shared, dev):
-    need = moe_experts_mxfp4_v41_workspace_size(T, K, E, H, I, has_shared)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    return workspace, workspace.numel() * workspace.element_size()
+_BF16 = (torch.bfloat16,)
 
 
 def moe_experts_mxfp4_v41(gate, up, down, n_experts, hidden, inter, x, topk_ids, topk_w,
@@ -219,10 +344,15 @@ def moe_experts_mxfp4_v41(gate, up, down, n_experts, hidden, inter, x, topk_ids,
                           stream=None):
     """V4.1 expert bank (bf16 x and out); with has_shared the banks hold
     n_experts + 1 experts, the shared one last."""
-    T, K = topk_ids.shape
+    _sizes(n_experts=n_experts)
+    d = _bank(gate, up, down, n_experts + int(bool(has_shared)), hidden, inter)
+    T, K, _ = _routing(topk_ids, d, topk_w)
+    _req(x, "x", _BF16, T * hidden, d)
     if out is None:
-        out = torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
-    ws, ws_bytes = _v41_ws(workspace, T, K, n_experts, hidden, inter, has_shared, x.device)
+        out = torch.empty((T, hidden), dtype=torch.bfloat16, device=d)
+    _req(out, "out", _BF16, T * hidden, d)
+    ws, ws_bytes = _ws(workspace, moe_experts_mxfp4_v41_workspace_size(
+        T, K, n_experts, hidden, inter, has_shared), d)
     _check(lib().moe_experts_mxfp4_v41(_ptr(gate), _ptr(up), _ptr(down), n_experts, hidden,
                                        inter, _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), K,
                                        float(swiglu_limit), int(has_shared), _ptr(out), _ptr(ws),
@@ -233,11 +363,36 @@ def moe_experts_mxfp4_v41(gate, up, down, n_experts, hidden, inter, x, topk_ids,
 def moe_experts_mxfp4_v41_stages(gate, up, down, n_experts, hidden, inter, x, topk_ids, topk_w,
                                  swiglu_limit=0.0, has_shared=False, out=None, workspace=None,
                                  h_in=None, h_out=None, stream=None):
-    T, K = topk_ids.shape
-    ws, ws_bytes = _v41_ws(workspace, T, K, n_experts, hidden, inter, has_shared, x.device)
+    _sizes(n_experts=n_experts)
+    sh = int(bool(has_shared))
+    d = _bank(gate, up, down, n_experts + sh, hidden, inter)
+    T, K, _ = _routing(topk_ids, d, topk_w)
+    _req(x, "x", _BF16, T * hidden, d)
+    if out is not None:
+        _req(out, "out", _BF16, T * hidden, d)
+    _h_buffers(h_in, h_out, T * (K + sh), inter, _BF16, d)
+    ws, ws_bytes = _ws(workspace, moe_experts_mxfp4_v41_workspace_size(
+        T, K, n_experts, hidden, inter, has_shared), d)
     _check(lib().moe_experts_mxfp4_v41_stages(_ptr(gate), _ptr(up), _ptr(down), n_experts,
                                               hidden, inter, _ptr(x), T, _ptr(topk_ids),
                                               _ptr(topk_w), K, float(swiglu_limit),
                                               int(has_shared), _ptr(out), _ptr(ws), ws_bytes,
                                               _ptr(h_in), _ptr(h_out), _stream(stream)))
     return out, h_out
+
+
+def mxfp4_probe_read(buf, nbytes=None, loads_per_thread=8, sink=None, stream=None):
+    """Measurement helper: one streaming read of ``nbytes`` bytes of ``buf``
+    (default: all of it).  Writes nothing."""
+    d = _req(buf, "buf", _U8)
+    _req_current(d)
+    nbytes = buf.numel() if nbytes is None else nbytes
+    _sizes(nbytes=nbytes, loads_per_thread=loads_per_thread)
+    if nbytes > buf.numel():
+        raise ValueError(f"buf: {buf.numel()} bytes, {nbytes} requested")
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device=d)
+    _req(sink, "sink", (torch.int32,), 1, d)
+    st = lib().mxfp4_probe_read(_ptr(buf), nbytes, loads_per_thread, _ptr(sink), _stream(stream))
+    if st != 0:
+        raise Mxfp4Error(st, "mxfp4_probe_read refused its arguments")

@@ -28,6 +28,13 @@
  *     message is available from mxfp4_last_error() (per thread).
  *   - There is no CPU fallback: every result is computed by HIP kernels.
  *   - Activations/outputs are row-major: x [b][cols], y [b][rows].
+ *   - Accuracy: weights are decoded exactly; fp32 activations enter the
+ *     matrix cores as two bf16 parts, hi = x truncated to bf16 and
+ *     lo = nearest bf16 of x - hi (|x - hi - lo| < 2^-15 |x|; any finite x,
+ *     up to the fp32 maximum); accumulation is fp32.  Every output is within
+ *     1e-4 * sum_c |W[r][c] * x[c]| of the exact product.  A NaN activation
+ *     or scale gives NaN outputs; an infinite fp32 activation gives NaN for
+ *     every output of its token (its low part is inf - inf).
  */
 #ifndef MXFP4_H
 #define MXFP4_H

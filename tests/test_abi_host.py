@@ -19,8 +19,8 @@ LIB = os.path.join(ROOT, "gemm_mxfp4_dequant_amd", "libmxfp4.so")
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmxfp4.so not built")
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?(?:int|int64_t|size_t|char)\s*\*?\s*(\w+)\s*\(", src,
                        flags=re.M)
@@ -40,6 +40,32 @@ def test_exports_every_declared_symbol(m):
     L = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_exports_every_symbol_of_every_header(m):
+    """Every header under include/ (the boundary and the measurement helper)
+    declares only functions the library exports."""
+    L = ctypes.CDLL(LIB)
+    inc = os.path.join(ROOT, "include")
+    seen = 0
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            for n in declared_functions(os.path.join(inc, h)):
+                assert hasattr(L, n), (h, n)
+                seen += 1
+    assert seen >= 14
+
+
+def test_probe_refusals(m):
+    f = ctypes.CDLL(LIB).mxfp4_probe_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    assert f(None, 1024, 8, FAKE, None) == -1
+    assert f(FAKE, 1000, 8, FAKE, None) == -1     # not a multiple of 16
+    assert f(FAKE, 1024, 5, FAKE, None) == -1     # loads per thread
+    assert f(FAKE + 8, 1024, 8, FAKE, None) == -1  # alignment
+    assert f(FAKE, 1024, 8, None, None) == -1
 
 
 def test_no_undefined_library_symbols():

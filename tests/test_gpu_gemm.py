@@ -182,3 +182,27 @@ def test_guard_band(m):
     hb = host(buf)
     assert np.all(hb[:32] == 777.0) and np.all(hb[-32:] == 777.0)
     assert not np.any(hb[32:-32] == 777.0)
+
+
+@pytest.mark.parametrize("rows,cols,b", [(64, 1024, 4), (12300, 512, 9)])
+def test_huge_and_infinite_activations(m, orc, rows, cols, b):
+    """fp32 activations beyond the bf16 range, up to the fp32 maximum (a
+    nearest-even bf16 of these would be infinite; the library's hi / lo
+    split truncates hi, so the products stay finite and within the
+    tolerance), and the documented behaviour of an infinite activation:
+    every output of its token is NaN.  Skinny kernel (64 rows) and tiled
+    kernel (12300 rows, b = 9)."""
+    w, x = inputs.gemm_case(25 + b, rows, cols, b, 118, 122)
+    x = x.copy()
+    x[0, 3] = np.float32(3.4e38)         # nearest bf16 overflows
+    x[0, 400] = np.float32(-3.4028235e38)  # fp32 maximum
+    x[1, 10] = np.float32(3.3e38)         # within the bf16 range
+    x[1, 11] = np.float32(3.3961514e38)   # exactly the bf16 overflow threshold
+    x[2, 5] = np.inf
+    x[3, 300] = -np.inf
+    y = run(m, w, rows, cols, x)
+    fin_tok = [t for t in range(b) if np.all(np.isfinite(x[t]))]
+    want, mag = orc.gemm(w, rows, cols, x[fin_tok])
+    assert np.all(np.isfinite(want[:2]))
+    assert_within(y[fin_tok], want, mag, what="huge finite activations")
+    assert np.all(np.isnan(y[2])) and np.all(np.isnan(y[3])), "infinite activation"
