@@ -14,7 +14,9 @@
 #include "../../include/mxfp4.h"
 #include "launch.h"
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 namespace {
 
@@ -140,6 +142,10 @@ struct MoeMode {
     bool shared;
 };
 
+// Stands for the static scratch in the argument checks of the allocation-
+// free expert bank (never dereferenced).
+void *const NOALLOC_WS = reinterpret_cast<void *>(uintptr_t(1));
+
 int check_moe(const void *gate, const void *up, const void *down, int64_t n_experts,
               int64_t hidden, int64_t inter, const void *x, int x_dtype, int64_t n_tokens,
               const int32_t *topk_ids, const float *topk_w, int64_t top_k, void *out,
@@ -168,14 +174,16 @@ int check_moe(const void *gate, const void *up, const void *down, int64_t n_expe
         TRY(check_dtype("out_dtype", out_dtype));
         TRY(check_buffer("out", out, 16));
     }
-    TRY(check_buffer("workspace", workspace, 16));
-    const size_t need = moe_layout(n_tokens, top_k, n_experts, hidden, inter, x_dtype).total;
-    if (workspace_bytes < need)
-        return fail(MXFP4_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
     const int64_t P = n_tokens * top_k;
     const int64_t nrb = ((hidden > inter ? hidden : inter) + 15) / 16; // smallest row block
     if (P * nrb > ((int64_t)1 << 31) - 1)
         return fail(MXFP4_EINVAL, "n_tokens * top_k * rows/16 too large for one launch");
+    if (workspace == NOALLOC_WS) // the static scratch: size checked by the caller
+        return MXFP4_OK;
+    TRY(check_buffer("workspace", workspace, 16));
+    const size_t need = moe_layout(n_tokens, top_k, n_experts, hidden, inter, x_dtype).total;
+    if (workspace_bytes < need)
+        return fail(MXFP4_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
     return MXFP4_OK;
 }
 
@@ -312,6 +320,52 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
     TRY(launched(mx::combine_launch(y, slot, mode.v41 ? nullptr : topk_w, (int)n_tokens,
                                     (int)top_k, (int)hidden, out, out_dtype == MXFP4_BF16, st),
                  "combine"));
+    return MXFP4_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free expert bank.  The array lives in the
+// library's device code (each GPU the library runs on holds its own copy
+// until the process ends); its device address is looked up once per device
+// with hipGetSymbolAddress, with that device current, and that address, never
+// the host-side name, is what the kernels receive.
+// ---------------------------------------------------------------------------
+constexpr size_t NOALLOC_SCRATCH_BYTES = MXFP4_NOALLOC_SCRATCH_BYTES;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::atomic<void *> g_scratch_ptr[NOALLOC_MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+} // namespace
+
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+int scratch_for_current_device(void **out)
+{
+    int dev = -1;
+    hipError_t st = hipGetDevice(&dev);
+    if (st != hipSuccess)
+        return fail(MXFP4_ELAUNCH, "hipGetDevice: %s", hipGetErrorString(st));
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+        return fail(MXFP4_EINVAL, "device %d: the static scratch serves devices 0..%d", dev,
+                    NOALLOC_MAX_DEVICES - 1);
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (!p) {
+            st = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (st != hipSuccess || !p)
+                return fail(MXFP4_ELAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                            hipGetErrorString(st));
+            if (reinterpret_cast<uintptr_t>(p) % 256 != 0)
+                return fail(MXFP4_EALIGN, "static scratch at %p is not 256-byte aligned", p);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
     return MXFP4_OK;
 }
 
@@ -488,6 +542,28 @@ int moe_experts_mxfp4(const void *gate, const void *up, const void *down, int64_
                   topk_w, top_k, out, out_dtype, true, workspace, workspace_bytes));
     return moe_run(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
                    topk_w, top_k, out, out_dtype, workspace, nullptr, nullptr, MoeMode{},
+                   (hipStream_t)stream);
+}
+
+int moe_experts_mxfp4_noalloc(const void *gate, const void *up, const void *down,
+                              int64_t n_experts, int64_t hidden, int64_t inter, const void *x,
+                              int x_dtype, int64_t n_tokens, const int32_t *topk_ids,
+                              const float *topk_w, int64_t top_k, void *out, int out_dtype,
+                              void *stream)
+{
+    clear_error();
+    TRY(check_moe(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
+                  topk_w, top_k, out, out_dtype, true, NOALLOC_WS, 0));
+    const size_t need = moe_layout(n_tokens, top_k, n_experts, hidden, inter, x_dtype).total;
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(MXFP4_EWORKSPACE,
+                    "these sizes need %zu bytes of scratch; the static scratch holds %zu "
+                    "(use moe_experts_mxfp4 with a workspace)",
+                    need, NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    TRY(scratch_for_current_device(&ws));
+    return moe_run(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
+                   topk_w, top_k, out, out_dtype, ws, nullptr, nullptr, MoeMode{},
                    (hipStream_t)stream);
 }
 

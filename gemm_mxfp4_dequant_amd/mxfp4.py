@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_size_t, P]),
         "moe_experts_mxfp4_stages": (I, [P, P, P, I64, I64, I64, P, I, I64, P, P, I64, P, I,
                                          P, ctypes.c_size_t, P, P, P]),
+        "moe_experts_mxfp4_noalloc": (I, [P, P, P, I64, I64, I64, P, I, I64, P, P, I64, P, I,
+                                          P]),
         "moe_experts_mxfp4_v41_workspace_size": (ctypes.c_size_t, [I64, I64, I64, I64, I64, I]),
         "moe_experts_mxfp4_v41": (I, [P, P, P, I64, I64, I64, P, I64, P, P, I64,
                                       ctypes.c_float, I, P, P, ctypes.c_size_t, P]),
@@ -306,6 +308,27 @@ def moe_experts_mxfp4(gate, up, down, n_experts, hidden, inter, x, topk_ids, top
     _check(lib().moe_experts_mxfp4(_ptr(gate), _ptr(up), _ptr(down), n_experts, hidden, inter,
                                    _ptr(x), _dt(x), T, _ptr(topk_ids), _ptr(topk_w), K, _ptr(out),
                                    _dt(out), _ptr(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+MXFP4_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_experts_mxfp4_noalloc(gate, up, down, n_experts, hidden, inter, x, topk_ids, topk_w,
+                              out, stream=None):
+    """moe_experts_mxfp4 on the library's static device scratch (no
+    workspace, nothing allocated by the library or here: ``out`` is the
+    caller's).  Sizes needing more than MXFP4_NOALLOC_SCRATCH_BYTES of
+    scratch are refused; calls that overlap on one GPU race."""
+    _sizes(n_experts=n_experts)
+    d = _bank(gate, up, down, n_experts, hidden, inter)
+    T, K, _ = _routing(topk_ids, d, topk_w)
+    _req(x, "x", _ACT, T * hidden, d)
+    _req(out, "out", _ACT, T * hidden, d)
+    _check(lib().moe_experts_mxfp4_noalloc(_ptr(gate), _ptr(up), _ptr(down), n_experts, hidden,
+                                           inter, _ptr(x), _dt(x), T, _ptr(topk_ids),
+                                           _ptr(topk_w), K, _ptr(out), _dt(out),
+                                           _stream(stream)))
     return out
 
 

@@ -155,6 +155,28 @@ int moe_experts_mxfp4(const void *gate, const void *up, const void *down, int64_
                       const int32_t *topk_ids, const float *topk_w, int64_t top_k, void *out,
                       int out_dtype, void *workspace, size_t workspace_bytes, void *stream);
 
+/* moe_experts_mxfp4 for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and result, bit for bit, with no workspace argument and no
+ * allocation of any kind.  The scratch it needs lives in a static device
+ * array of MXFP4_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends; its address is looked up on the first call on
+ * each device (that device current).  Sizes whose workspace query exceeds
+ * MXFP4_NOALLOC_SCRATCH_BYTES are refused with MXFP4_EWORKSPACE before
+ * anything is launched (the 64-expert decode layer needs about 1.2 MB; a
+ * 512-token prefill of 7168 x 2048 experts at top 8 needs 134 MB and does
+ * not fit).  Every call on a GPU uses that GPU's one array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  The scratch needs no clearing between calls
+ * (every call writes each part before reading it).  Other errors as
+ * moe_experts_mxfp4. */
+#define MXFP4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_experts_mxfp4_noalloc(const void *gate, const void *up, const void *down,
+                              int64_t n_experts, int64_t hidden, int64_t inter, const void *x,
+                              int x_dtype, int64_t n_tokens, const int32_t *topk_ids,
+                              const float *topk_w, int64_t top_k, void *out, int out_dtype,
+                              void *stream);
+
 /* Stage-isolation variant of moe_experts_mxfp4 (the gs_in / gs_out hooks of
  * "cortiq-engine 0.8.77, src/qtensor/moe_fast.rs", run_stages).  h is in
  * SLOT order ([n_tokens*top_k][inter] of x_dtype, slot as returned by

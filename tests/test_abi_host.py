@@ -36,7 +36,7 @@ def m():
 
 def test_exports_every_declared_symbol(m):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     L = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(L, n), n
@@ -205,3 +205,23 @@ def test_group_refusals(m):
     assert L.moe_route_group(FAKE, 4, 2, 0, FAKE, FAKE, FAKE, None) == m.MXFP4_EINVAL
     assert L.moe_route_group(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, None) == m.MXFP4_EINVAL
     assert L.moe_route_group(FAKE + 1, 4, 2, 8, FAKE, FAKE, FAKE, None) == m.MXFP4_EALIGN
+
+
+def test_noalloc_refusals_before_any_launch():
+    """The allocation-free expert bank refuses, on the host and before any
+    HIP call, sizes whose scratch exceeds its static array, and the usual
+    bad arguments."""
+    L = ctypes.CDLL(LIB)
+    f = L.moe_experts_mxfp4_noalloc
+    f.restype = ctypes.c_int
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    f.argtypes = [P, P, P, I64, I64, I64, P, I, I64, P, P, I64, P, I, P]
+    err = L.mxfp4_last_error
+    err.restype = ctypes.c_char_p
+    # the 512-token prefill layer: 134 MB of scratch
+    assert f(FAKE, FAKE, FAKE, 256, 7168, 2048, FAKE, 1, 512, FAKE, FAKE, 8, FAKE, 1, None) == -3
+    assert b"static scratch" in err()
+    assert f(FAKE, FAKE, FAKE, 0, 4096, 2048, FAKE, 0, 8, FAKE, FAKE, 6, FAKE, 1, None) == -1
+    assert f(FAKE, FAKE, FAKE, 64, 4096, 2048, FAKE, 0, 8, FAKE, FAKE, 6, None, 1, None) == -1
+    assert f(FAKE, FAKE, FAKE, 64, 4096, 2048, FAKE + 4, 0, 8, FAKE, FAKE, 6, FAKE, 1,
+             None) == -2

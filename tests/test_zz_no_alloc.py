@@ -1,0 +1,85 @@
+"""The allocation-free expert bank (moe_experts_mxfp4_noalloc: the static
+device scratch instead of a caller workspace) against moe_experts_mxfp4 with
+a workspace, through the C ABI: the same kernels in the same order, so the
+outputs must be equal bit for bit.  Two calls in a row on the one static
+scratch, the second with fewer tokens (and then the first again), so a call
+that read anything the previous call left behind would differ.  The first
+bank's output is also checked against the oracle (end-to-end nrmse / cos,
+as the expert-bank tests do)."""
+import numpy as np
+import pytest
+import torch
+
+from gemm_mxfp4_dequant_amd import inputs
+from tests.helpers import bf16_to_f64, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    from gemm_mxfp4_dequant_amd import mxfp4
+    mxfp4.lib()
+    return mxfp4
+
+
+def upload(c):
+    return {k: dev(v) for k, v in c.items()}
+
+
+def with_ws(m, d, E, H, I):
+    return host(m.moe_experts_mxfp4(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"],
+                                    d["w"]))
+
+
+def no_alloc(m, d, E, H, I):
+    T = d["ids"].shape[0]
+    out = torch.full((T, H), 7.0, dtype=torch.bfloat16, device="cuda")
+    m.moe_experts_mxfp4_noalloc(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"],
+                                d["w"], out)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("xd", ["f32", "bf16"])
+def test_noalloc_equals_workspace_bank(m, orc, xd):
+    E, H, I = 16, 4096, 2048
+    big = inputs.moe_case(61, E, H, I, 8, 6, xd, "softmax", scale_lo=100, scale_hi=114)
+    small = dict(big)
+    small["x"], small["ids"], small["w"] = big["x"][:3], big["ids"][:3], big["w"][:3]
+    db, ds = upload(big), upload(small)
+    ref_b, ref_s = with_ws(m, db, E, H, I), with_ws(m, ds, E, H, I)
+    got_b = no_alloc(m, db, E, H, I)
+    got_s = no_alloc(m, ds, E, H, I)
+    got_b2 = no_alloc(m, db, E, H, I)
+    assert np.array_equal(got_b, ref_b), "first call"
+    assert np.array_equal(got_s, ref_s), "second, smaller call"
+    assert np.array_equal(got_b2, ref_b), "the first shape again"
+    # and the bank itself against the oracle (both sides rounded to bf16)
+    ref = orc.moe(big["gate"], big["up"], big["down"], E, H, I, big["x"], big["ids"], big["w"],
+                  xd == "bf16")
+    want = bf16_to_f64(ref["out_bf16"])
+    got = bf16_to_f64(got_b)
+    nrmse = np.sqrt(np.mean((got - want) ** 2)) / np.sqrt(np.mean(want ** 2))
+    cos = float((got * want).sum() / np.sqrt((got * got).sum() * (want * want).sum()))
+    assert nrmse < 1e-3 and cos > 0.9999, (nrmse, cos)
+
+
+def test_noalloc_refuses_sizes_beyond_the_scratch(m):
+    """A bank whose workspace would exceed the static scratch is refused
+    before any launch, and the output is left untouched."""
+    E, H, I, T, K = 4, 4096, 512, 1024, 4   # y alone: 4096 pairs x 4096 x 4 B = 64 MiB
+    need = m.moe_experts_mxfp4_workspace_size(T, K, E, H, I, torch.float32)
+    assert need > m.MXFP4_NOALLOC_SCRATCH_BYTES
+    nb = I * H // 2 + I * H // 32
+    bank = torch.zeros(E * nb, dtype=torch.uint8, device="cuda")
+    ids = torch.zeros((T, K), dtype=torch.int32, device="cuda")
+    w = torch.full((T, K), 0.25, device="cuda")
+    x = torch.zeros((T, H), device="cuda")
+    out = torch.full((T, H), 3.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(m.Mxfp4Error) as e:
+        m.moe_experts_mxfp4_noalloc(bank, bank, bank, E, H, I, x, ids, w, out)
+    assert e.value.status == m.MXFP4_EWORKSPACE
+    assert "static scratch" in str(e.value)
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
