@@ -58,6 +58,8 @@ def _load():
     lib.orc_dequant_bf16.argtypes = [P, I64, I64, P]
     lib.orc_bf16_rne.restype = ctypes.c_uint16
     lib.orc_bf16_rne.argtypes = [ctypes.c_double]
+    lib.orc_bf16_rne_n.restype = None
+    lib.orc_bf16_rne_n.argtypes = [P, I64, P]
     lib.orc_gemm.restype = None
     lib.orc_gemm.argtypes = [P, I64, I64, P, I64, P, P, ctypes.c_int]
     lib.orc_gemm_rows.restype = None
@@ -155,9 +157,11 @@ def bf16_rne(v: float) -> int:
 
 
 def bf16_rne_array(a) -> np.ndarray:
-    a = np.asarray(a, dtype=np.float64).reshape(-1)
-    f = _load().orc_bf16_rne
-    return np.fromiter((f(float(v)) for v in a), dtype=np.uint16, count=a.size)
+    """bf16_rne of every element (flattened), as uint16 bit patterns."""
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64).reshape(-1))
+    out = np.empty(a.size, np.uint16)
+    _load().orc_bf16_rne_n(_ptr(a), a.size, _ptr(out))
+    return out
 
 
 def bf16_bits_to_f64(bits) -> np.ndarray:
@@ -323,6 +327,75 @@ def moe(gate, up, down, n_experts, hidden, inter, x, topk_ids, topk_w, round_h_b
     out, mag_out = moe_combine(y, mag_y, topk_w, topk_ids, n_experts)
     st.update(y=y, mag_y=mag_y, out=out, mag_out=mag_out, out_bf16=bf16_rne_array(out).reshape(out.shape))
     return st
+
+
+# --------------------------------------------------------------------------
+# Dense form of the expert stages: the method's plain definition written out
+# per expert (dequantize the expert's tensors exactly, then dense fp64
+# products of the routed rows), with numpy's fp64 matrix product as the
+# library step.  Same results as moe_gate_up / moe_down up to fp64 rounding
+# (pinned against them in test_oracle_moe), but each expert is decoded once
+# instead of once per pair, so full-size layers can be checked pair by pair
+# in seconds.  Valid when no weight overflows fp32 (scale bytes up to 252;
+# asserted); a scale of 255 gives NaN rows as in the loop form.
+# --------------------------------------------------------------------------
+
+def _expert_f64(bank, e, rows, cols):
+    nb = nbytes(rows, cols)
+    wf = dequant_f32(bank[e * nb:(e + 1) * nb], rows, cols)
+    assert not np.isinf(wf).any(), "dense oracle form: a weight overflows fp32"
+    return wf.astype(np.float64)
+
+
+def moe_gate_up_dense(gate, up, n_experts, hidden, inter, x, topk_ids, round_h_bf16):
+    """moe_gate_up in dense form (see above): the same dict, [P, inter]
+    each, rows of pairs with invalid ids left at 0.  Pinned against
+    moe_gate_up in test_oracle_moe."""
+    x = _as_f64(x)
+    ids = _sanitize_ids(topk_ids, n_experts)
+    T, K = ids.shape
+    P = T * K
+    gate = _as_bytes(gate)
+    up = _as_bytes(up)
+    assert x.shape == (T, hidden)
+    out = {k: np.zeros((P, inter), np.float64) for k in ("g", "u", "h", "mag_g", "mag_u")}
+    flat = ids.reshape(-1)
+    for e in np.unique(flat[flat >= 0]):
+        pe = np.where(flat == e)[0]
+        xe = x[pe // K]
+        for name, bank in (("g", gate), ("u", up)):
+            W = _expert_f64(bank, int(e), inter, hidden)
+            out[name][pe] = xe @ W.T
+            out["mag_" + name][pe] = np.abs(xe) @ np.abs(W).T
+    g, u = out["g"], out["u"]
+    with np.errstate(over="ignore"):
+        h = g / (1.0 + np.exp(-g)) * u
+    if round_h_bf16:
+        h = bf16_bits_to_f64(bf16_rne_array(h)).reshape(h.shape)
+    h[flat < 0] = 0.0
+    out["h"] = h
+    return out
+
+
+def moe_down_dense(down, n_experts, hidden, inter, h, topk_ids):
+    """moe_down in dense form: y[p] = W_down[e_p] . h[p] and its magnitudes,
+    [P, hidden] fp64 (zeros for pairs with invalid ids).  Pinned against
+    moe_down in test_oracle_moe."""
+    ids = _sanitize_ids(topk_ids, n_experts)
+    T, K = ids.shape
+    P = T * K
+    h = _as_f64(h)
+    down = _as_bytes(down)
+    assert h.shape == (P, inter)
+    y = np.zeros((P, hidden), np.float64)
+    mag = np.zeros((P, hidden), np.float64)
+    flat = ids.reshape(-1)
+    for e in np.unique(flat[flat >= 0]):
+        pe = np.where(flat == e)[0]
+        W = _expert_f64(down, int(e), hidden, inter)
+        y[pe] = h[pe] @ W.T
+        mag[pe] = np.abs(h[pe]) @ np.abs(W).T
+    return y, mag
 
 
 def moe_v41_act(g, u, topk_w, topk_ids, n_experts, swiglu_limit):

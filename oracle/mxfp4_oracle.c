@@ -163,6 +163,13 @@ uint16_t orc_bf16_rne(double v)
     return sign | (uint16_t)(bits >> 16);
 }
 
+/* orc_bf16_rne over an array (the same rounding, element by element). */
+void orc_bf16_rne_n(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_bf16_rne(v[i]);
+}
+
 /* Bit pattern of a weight in bf16: the fp32 value is exact with at most two
  * significant bits, so it is its own bf16 rounding. */
 void orc_dequant_bf16(const uint8_t *w, int64_t rows, int64_t cols, uint16_t *out)

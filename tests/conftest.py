@@ -17,3 +17,11 @@ def orc():
     import oracle
     oracle._load()
     return oracle
+
+
+@pytest.fixture(scope="session")
+def prefill_case():
+    """The 256-expert prefill workload's inputs (about 6 GB of weights), drawn
+    once per session for the tests that check it at full size."""
+    from gemm_mxfp4_dequant_amd import inputs
+    return inputs.workload_case(5)

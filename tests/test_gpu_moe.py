@@ -12,8 +12,9 @@
   bf16 rounding alone is ~1.1e-3 rms);
 * invariants: reruns are bitwise equal; out-of-range ids drop pairs.
 Workloads: small banks (ragged sizes, scales in the SwiGLU's curved region),
-the 64-expert decode layer at full size, and the 256-expert prefill layer at
-full size with sampled tokens.
+the 64-expert decode layer at full size (every output), and the 256-expert
+prefill layer at full size (h of every pair of the three most-routed
+experts, down + combine on 32+ tokens).
 """
 import numpy as np
 import pytest
@@ -56,7 +57,13 @@ def gpu_stages(m, d, E, H, I, xbf):
     return host(h), host(offs), host(pos), host(slot)
 
 
-def check_case(m, orc, c, E, H, I, xbf, sample_pairs=None, e2e=True):
+def check_case(m, orc, c, E, H, I, xbf, sample_pairs=None, e2e=True, tokens=None,
+               e2e_tokens=None, dense=False):
+    """Stage-isolated checks of one bank: h for the pairs ``sample_pairs``
+    (all pairs if None), down + combine for ``tokens`` (default: the tokens
+    of the checked pairs), end to end for ``e2e_tokens`` (default: the same
+    tokens).  ``dense`` computes the oracle's gate/up in its dense form (one
+    decode per expert; for many pairs on few experts)."""
     T, K = c["ids"].shape
     P = T * K
     d = upload(c)
@@ -74,7 +81,8 @@ def check_case(m, orc, c, E, H, I, xbf, sample_pairs=None, e2e=True):
         keep[sample_pairs] = True
         ids_s[~keep] = -1
     ids_s = ids_s.reshape(T, K)
-    st = orc.moe_gate_up(c["gate"], c["up"], E, H, I, c["x"], ids_s, xbf)
+    gate_up = orc.moe_gate_up_dense if dense else orc.moe_gate_up
+    st = gate_up(c["gate"], c["up"], E, H, I, c["x"], ids_s, xbf)
     flat = ids_s.reshape(-1)
     valid = np.where((flat >= 0) & (flat < E))[0]
     hp = h_gpu[slot[valid]]
@@ -93,7 +101,10 @@ def check_case(m, orc, c, E, H, I, xbf, sample_pairs=None, e2e=True):
     h_pair = np.zeros((P, I))
     vv = np.where(slot >= 0)[0]
     h_pair[vv] = (bf16_to_f64(h_gpu[slot[vv]]) if xbf else h_gpu[slot[vv]].astype(np.float64))
-    tok = np.unique(valid // K) if sample_pairs is not None else np.arange(T)
+    if tokens is None:
+        tok = np.unique(valid // K) if sample_pairs is not None else np.arange(T)
+    else:
+        tok = np.asarray(tokens)
     ids_t = np.full_like(c["ids"], -1)
     ids_t[tok] = c["ids"][tok]
     y, mag_y = orc.moe_down(c["down"], E, H, I, h_pair, ids_t)
@@ -103,16 +114,40 @@ def check_case(m, orc, c, E, H, I, xbf, sample_pairs=None, e2e=True):
     if e2e:
         out2 = m.moe_experts_mxfp4(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"], d["w"])
         out2 = bf16_to_f64(host(out2))
+        te = tok if e2e_tokens is None else np.asarray(e2e_tokens)
         ids_e = np.full_like(c["ids"], -1)
-        ids_e[tok] = c["ids"][tok]
+        ids_e[te] = c["ids"][te]
         # both sides rounded to bf16 (the oracle once, from fp64)
         ref = orc.moe(c["gate"], c["up"], c["down"], E, H, I, c["x"], ids_e, c["w"], xbf)
-        ref = bf16_to_f64(ref["out_bf16"])[tok]
-        got = out2[tok]
+        ref = bf16_to_f64(ref["out_bf16"])[te]
+        got = out2[te]
         nrmse = np.sqrt(np.mean((got - ref) ** 2)) / np.sqrt(np.mean(ref ** 2))
         cos = float((got * ref).sum() / np.sqrt((got * got).sum() * (ref * ref).sum()))
         assert nrmse < 1e-3 and cos > 0.9999, (nrmse, cos)
         return out2
+
+
+def hot_expert_sample(ids, n_experts, n_hot=3, tpi=64, n_tokens=32, seed=0):
+    """Pairs and tokens for a full-size check of a skewed routing: every pair
+    (slot) of the ``n_hot`` most-routed experts, so every work item of up to
+    ``tpi`` tokens and every position in those items is checked; and at
+    least ``n_tokens`` tokens: the first and last token of each such item,
+    filled up with seeded random tokens."""
+    T, K = ids.shape
+    flat = ids.reshape(-1)
+    cnt = np.bincount(flat[(flat >= 0) & (flat < n_experts)], minlength=n_experts)
+    hot = np.argsort(-cnt, kind="stable")[:n_hot]
+    pairs = np.where(np.isin(flat, hot))[0]
+    toks = set()
+    for e in hot:
+        pe = np.where(flat == e)[0]          # the expert's slots, in pair order
+        for i0 in range(0, pe.size, tpi):
+            item = pe[i0:i0 + tpi]
+            toks.update((int(item[0] // K), int(item[-1] // K)))
+    rng = np.random.default_rng(seed)
+    while len(toks) < n_tokens:
+        toks.add(int(rng.integers(T)))
+    return hot, cnt[hot], pairs, np.array(sorted(toks))
 
 
 @pytest.mark.parametrize("xd", ["f32", "bf16"])
@@ -167,15 +202,19 @@ def test_workload4_decode_full(m, orc):
     check_case(m, orc, c, cfg["n_experts"], cfg["hidden"], cfg["inter"], False)
 
 
-def test_workload5_prefill_sampled(m, orc):
+def test_workload5_prefill_hot_experts(m, orc, prefill_case):
+    """The 256-expert prefill layer at full size: h of every pair of the three
+    most-routed experts (441, 321 and 236 pairs in this draw: every 64-token
+    work item and every position in it), down + combine on 32+ tokens (the
+    first and last token of each of those items, and random ones), end to
+    end on 8 of them."""
     cfg = inputs.WORKLOADS[5]
-    c = inputs.workload_case(5)
-    T, K = c["ids"].shape
-    rng = np.random.default_rng(5)
-    toks = rng.choice(T, 3, replace=False)
-    pairs = np.concatenate([t * K + np.arange(K) for t in toks])
+    c = prefill_case
+    hot, counts, pairs, toks = hot_expert_sample(c["ids"], cfg["n_experts"])
+    assert counts.min() > 64 and len(toks) >= 32
     check_case(m, orc, c, cfg["n_experts"], cfg["hidden"], cfg["inter"], True,
-               sample_pairs=pairs)
+               sample_pairs=pairs, tokens=toks, e2e_tokens=toks[::max(1, len(toks) // 8)],
+               dense=True)
 
 
 def test_rerun_bitwise(m):

@@ -50,7 +50,12 @@ def run(m, d, E, H, I, lim, shared, **kw):
                                    d["w"], swiglu_limit=lim, has_shared=shared, **kw)
 
 
-def check(m, orc, c, E, H, I, lim, shared, tokens=None):
+def check(m, orc, c, E, H, I, lim, shared, tokens=None, pairs=None, e2e_tokens=None,
+          dense=False):
+    """h for the augmented-routing pairs ``pairs`` (default: every pair of
+    ``tokens``, or of all tokens), down + combine for ``tokens``, end to end
+    for ``e2e_tokens`` (default: ``tokens``).  ``dense``: the oracle's
+    gate/up in its dense form."""
     T, K = c["ids"].shape
     d = {k: dev(v) for k, v in c.items()}
     ids_a, w_a, Ea = orc.v41_routing(c["ids"], c["w"], E, shared)
@@ -60,6 +65,12 @@ def check(m, orc, c, E, H, I, lim, shared, tokens=None):
     keep = np.zeros(T, bool)
     keep[tok] = True
     ids_k = np.where(keep[:, None], ids_a, -1).astype(np.int32)
+    if pairs is None:
+        ids_h = ids_k
+    else:
+        flat = np.full(Pa, -1, np.int32)
+        flat[pairs] = ids_a.reshape(-1)[pairs]
+        ids_h = flat.reshape(T, Ka)
 
     # stage isolation: h in slot order of the augmented routing
     h = torch.empty((Pa, I), dtype=torch.bfloat16, device="cuda")
@@ -68,9 +79,10 @@ def check(m, orc, c, E, H, I, lim, shared, tokens=None):
     _, _, slot = m.moe_route_group(dev(ids_a), Ea)
     slot = host(slot)
     h_gpu = host(h)
-    st = orc.moe_gate_up(c["gate"], c["up"], Ea, H, I, c["x"], ids_k, False)
-    h_or = orc.moe_v41_act(st["g"], st["u"], w_a, ids_k, Ea, lim)
-    flat = ids_k.reshape(-1)
+    gate_up = orc.moe_gate_up_dense if dense else orc.moe_gate_up
+    st = gate_up(c["gate"], c["up"], Ea, H, I, c["x"], ids_h, False)
+    h_or = orc.moe_v41_act(st["g"], st["u"], w_a, ids_h, Ea, lim)
+    flat = ids_h.reshape(-1)
     valid = np.where((flat >= 0) & (flat < Ea))[0]
     hp = bf16_to_f64(h_gpu[slot[valid]])
     g, u = st["g"][valid], st["u"][valid]
@@ -102,11 +114,12 @@ def check(m, orc, c, E, H, I, lim, shared, tokens=None):
     assert_within(out_g[tok], o[tok], mag_o[tok], extra=ulp_bf16(o[tok]), what="down+combine")
 
     # end to end against the oracle's own chain
+    te = tok if e2e_tokens is None else np.asarray(e2e_tokens)
     out2 = bf16_to_f64(host(run(m, d, E, H, I, lim, shared)))
-    ref = orc.moe_v41(c["gate"], c["up"], c["down"], E, H, I, c["x"][tok], c["ids"][tok],
-                      c["w"][tok], lim, shared)
+    ref = orc.moe_v41(c["gate"], c["up"], c["down"], E, H, I, c["x"][te], c["ids"][te],
+                      c["w"][te], lim, shared)
     ref = bf16_to_f64(ref["out_bf16"])
-    got = out2[tok]
+    got = out2[te]
     nrmse = np.sqrt(np.mean((got - ref) ** 2)) / np.sqrt(np.mean(ref ** 2))
     cos = float((got * ref).sum() / np.sqrt((got * got).sum() * (ref * ref).sum()))
     assert nrmse < 2e-3 and cos > 0.9999, (nrmse, cos)
@@ -149,22 +162,28 @@ def test_max_experts_shared_with_dropped_ids(m, orc, T):
     check(m, orc, c, E, H, I, 1.0, True)
 
 
-def test_prefill_shape_sampled(m, orc):
-    """The 256-expert prefill layer with a shared expert and limit 10, a few
-    tokens checked (full-size run)."""
+def test_prefill_shape_hot_experts(m, orc, prefill_case):
+    """The 256-expert prefill layer at full size with a shared expert and
+    limit 10: h of every pair of the three most-routed experts of the
+    augmented routing (the shared expert, on all 512 tokens, and the two
+    hottest routed ones: every 64-token work item and position), down +
+    combine on 32+ tokens (first and last token of each of those items, and
+    random ones), end to end on 8 of them."""
+    from tests.test_gpu_moe import hot_expert_sample
     cfg = inputs.WORKLOADS[5]
-    E, H, I, T, K = (cfg["n_experts"], cfg["hidden"], cfg["inter"], cfg["n_tokens"],
-                     cfg["top_k"])
-    c = inputs.workload_case(5)
+    E, H, I = cfg["n_experts"], cfg["hidden"], cfg["inter"]
     rng = inputs.rng_for(55)
     sh = [inputs.draw_weights(rng, I, H, cfg["scale_lo"], cfg["scale_hi"]),
           inputs.draw_weights(rng, I, H, cfg["scale_lo"], cfg["scale_hi"]),
           inputs.draw_weights(rng, H, I, cfg["scale_lo"], cfg["scale_hi"])]
-    c = dict(c)
+    c = dict(prefill_case)
     for k, s in zip(("gate", "up", "down"), sh):
         c[k] = np.concatenate([c[k], s])
-    toks = np.random.default_rng(6).choice(T, 3, replace=False)
-    check(m, orc, c, E, H, I, 10.0, True, tokens=toks)
+    ids_a, _, Ea = orc.v41_routing(c["ids"], c["w"], E, True)
+    hot, counts, pairs, toks = hot_expert_sample(ids_a, Ea)
+    assert hot[0] == E and counts.min() > 64 and len(toks) >= 32
+    check(m, orc, c, E, H, I, 10.0, True, tokens=toks, pairs=pairs,
+          e2e_tokens=toks[::max(1, len(toks) // 8)], dense=True)
 
 
 def test_token_alone_equals_batch_bitwise(m):

@@ -140,3 +140,50 @@ def test_weights_scale_output(orc):
     r2 = orc.moe(c["gate"], c["up"], c["down"], E, H, I, c["x"], c["ids"], c["w"] * 2, False)
     assert np.array_equal(r2["out"], 2 * r1["out"])
     assert np.array_equal(r2["mag_out"], 2 * r1["mag_out"])
+
+
+@pytest.mark.parametrize("xd,round_h", [("f32", False), ("bf16", True), ("bf16", False)])
+def test_dense_form_equals_loop_form(orc, xd, round_h):
+    """The dense form of the expert stages (each expert dequantized once,
+    fp64 matrix products) against the loop form, which the tests above pin:
+    g, u, y and their magnitudes within fp64 rounding of the magnitude sums,
+    h (and its bf16 rounding) alike, dropped pairs zero in both, NaN rows
+    where a scale byte is 255."""
+    E, H, I, T, K = 6, 256, 160, 9, 3
+    c = inputs.moe_case(301, E, H, I, T, K, xd, "softmax", scale_lo=100, scale_hi=130)
+    ids = c["ids"].copy()
+    ids[2, 1] = -1
+    ids[5, 0] = E + 2
+    nb = orc.nbytes(I, H)
+    gate = c["gate"].copy()
+    gate[2 * nb + I * H // 2 + 3 * (H // 32) + 1] = 255   # expert 2, row 3, group 1
+    lf = orc.moe_gate_up(gate, c["up"], E, H, I, c["x"], ids, round_h)
+    df = orc.moe_gate_up_dense(gate, c["up"], E, H, I, c["x"], ids, round_h)
+    # each quantity within 1e-12 of its own magnitude sum (fp64 rounding of
+    # sums in a different order); h through silu(g) u of those
+    scales = {"g": lf["mag_g"], "u": lf["mag_u"], "mag_g": lf["mag_g"], "mag_u": lf["mag_u"],
+              "h": lf["mag_g"] * np.abs(lf["u"]) + lf["mag_u"] + np.abs(lf["h"])}
+    for k in ("g", "u", "h", "mag_g", "mag_u"):
+        a, b = lf[k], df[k]
+        assert np.array_equal(np.isnan(a), np.isnan(b)), k
+        ok = ~np.isnan(a)
+        assert np.all(np.abs(a[ok] - b[ok]) <= 1e-12 * scales[k][ok] + 1e-300), k
+    assert np.isnan(lf["g"]).any() and not np.isnan(lf["u"]).any()
+    assert np.all(df["g"][[2 * K + 1, 5 * K + 0]] == 0)
+    if round_h:
+        fin = np.isfinite(lf["h"])
+        assert np.array_equal(lf["h"][fin], df["h"][fin])
+    h = np.where(np.isnan(lf["h"]), 0.0, lf["h"])
+    y1, m1 = orc.moe_down(c["down"], E, H, I, h, ids)
+    y2, m2 = orc.moe_down_dense(c["down"], E, H, I, h, ids)
+    assert np.all(np.abs(y1 - y2) <= 1e-12 * m1 + 1e-300)
+    assert np.all(np.abs(m1 - m2) <= 1e-12 * m1 + 1e-300)
+
+
+def test_dense_form_refuses_overflowing_weights(orc):
+    """Scale 254 with |code| >= 2 overflows fp32: the dense form (built on
+    the fp32 dequantization) refuses rather than return inf products."""
+    E, H, I, T, K = 2, 64, 32, 2, 1
+    c = inputs.moe_case(302, E, H, I, T, K, "f32", "softmax", scale_lo=254, scale_hi=254)
+    with pytest.raises(AssertionError, match="overflows"):
+        orc.moe_gate_up_dense(c["gate"], c["up"], E, H, I, c["x"], c["ids"], False)
