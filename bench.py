@@ -473,7 +473,41 @@ def main():
                                                                 1),
                                    **spread_us(t, 30)}
         log(f"moe_decode_e64: {extra['moe_decode_e64']}")
-        del s, t
+        # the same layer with its four most-routed experts in pinned host
+        # memory (moe_experts_mxfp4_ptrs: their weights cross the host link
+        # on every step; the other experts stay in device memory)
+        import numpy as np
+        cfg = inputs.WORKLOADS[4]
+        E, H, I = cfg["n_experts"], cfg["hidden"], cfg["inter"]
+        ids_h = s["ids"].cpu().numpy()
+        hot = set(int(e) for e in np.argsort(-np.bincount(ids_h.reshape(-1), minlength=E),
+                                             kind="stable")[:4])
+        bk = s["bank"][0]
+        tabs = []
+        keep = []
+        for r, (rows_, cols_) in enumerate(((I, H), (I, H), (H, I))):
+            ts = []
+            for e in range(E):
+                if e in hot:
+                    tp = torch.empty(bk[r][e].numel(), dtype=torch.uint8, pin_memory=True)
+                    tp.copy_(bk[r][e])
+                    ts.append(tp)
+                else:
+                    ts.append(bk[r][e])
+            keep.append(ts)
+            tabs.append(mx.expert_table(ts, rows_, cols_))
+        hb = sum(3 * tensor_bytes(I, H) for e in hot if e in set(ids_h.reshape(-1).tolist()))
+        L = [lambda: mx.moe_experts_mxfp4_ptrs(tabs[0], tabs[1], tabs[2], E, H, I, s["x"],
+                                               s["ids"], s["w"], out=s["out"], workspace=s["ws"])]
+        t2 = Timer(torch, L, args.eager, passes=8)
+        ms2 = t2.time(16)
+        extra["moe_decode_e64_host4"] = {"us_per_layer": round(ms2 * 1e3, 2),
+                                         "tok_per_s": round(s["T"] / (ms2 * 1e-3), 1),
+                                         "host_experts": sorted(hot),
+                                         "host_bytes": hb,
+                                         "host_GBps": round(hb / ms2 / 1e6, 2)}
+        log(f"moe_decode_e64_host4: {extra['moe_decode_e64_host4']}")
+        del s, t, t2, L, tabs, keep
         # the device router on the routing sizes of both layers (outside the
         # layer's own timing: the layer takes its routing as input)
         for name, (T, E, K) in (("route_topk_8x64_k6", (8, 64, 6)),

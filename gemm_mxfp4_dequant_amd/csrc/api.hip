@@ -140,16 +140,36 @@ struct MoeMode {
     bool v41;
     float lim;
     bool shared;
+    bool tables; // gate / up / down are per-expert pointer tables
 };
 
 // Stands for the static scratch in the argument checks of the allocation-
 // free expert bank (never dereferenced).
 void *const NOALLOC_WS = reinterpret_cast<void *>(uintptr_t(1));
 
+// A table of per-expert tensor pointers (device array, 8-byte aligned) for
+// rows x cols experts: the table itself and the shape are checked here; its
+// entries are device data.
+int check_table(const char *name, const void *t, int64_t rows, int64_t cols)
+{
+    TRY(check_buffer(name, t, 8));
+    if (rows < 1 || rows > MXFP4_MAX_ROWS)
+        return fail(MXFP4_EINVAL, "%s: rows = %lld outside [1, %d]", name, (long long)rows,
+                    MXFP4_MAX_ROWS);
+    if (cols < 32 || cols > MXFP4_MAX_COLS || cols % 32 != 0)
+        return fail(MXFP4_EINVAL, "%s: cols = %lld must be a multiple of 32 in [32, %d]", name,
+                    (long long)cols, MXFP4_MAX_COLS);
+    if (mxfp4_nbytes(rows, cols) > MXFP4_MAX_TENSOR_BYTES)
+        return fail(MXFP4_EINVAL, "%s: %lld x %lld exceeds %lld bytes", name, (long long)rows,
+                    (long long)cols, (long long)MXFP4_MAX_TENSOR_BYTES);
+    return MXFP4_OK;
+}
+
 int check_moe(const void *gate, const void *up, const void *down, int64_t n_experts,
               int64_t hidden, int64_t inter, const void *x, int x_dtype, int64_t n_tokens,
               const int32_t *topk_ids, const float *topk_w, int64_t top_k, void *out,
-              int out_dtype, bool need_out, void *workspace, size_t workspace_bytes)
+              int out_dtype, bool need_out, void *workspace, size_t workspace_bytes,
+              bool tables = false)
 {
     if (n_experts < 1 || n_experts > MXFP4_MAX_EXPERTS)
         return fail(MXFP4_EINVAL, "n_experts = %lld outside [1, %d]", (long long)n_experts,
@@ -160,10 +180,16 @@ int check_moe(const void *gate, const void *up, const void *down, int64_t n_expe
     if (n_tokens < 1 || n_tokens > MXFP4_MAX_TOKENS)
         return fail(MXFP4_EINVAL, "n_tokens = %lld outside [1, %d]", (long long)n_tokens,
                     MXFP4_MAX_TOKENS);
-    TRY(check_tensor("gate", gate, inter, hidden));
-    TRY(check_tensor("up", up, inter, hidden));
-    TRY(check_tensor("down", down, hidden, inter));
-    if (mxfp4_nbytes(inter, hidden) % 16 != 0)
+    if (tables) {
+        TRY(check_table("gate", gate, inter, hidden));
+        TRY(check_table("up", up, inter, hidden));
+        TRY(check_table("down", down, hidden, inter));
+    } else {
+        TRY(check_tensor("gate", gate, inter, hidden));
+        TRY(check_tensor("up", up, inter, hidden));
+        TRY(check_tensor("down", down, hidden, inter));
+    }
+    if (!tables && mxfp4_nbytes(inter, hidden) % 16 != 0)
         return fail(MXFP4_EALIGN, "expert tensor size %lld is not a multiple of 16 bytes",
                     (long long)mxfp4_nbytes(inter, hidden));
     TRY(check_dtype("x_dtype", x_dtype));
@@ -277,6 +303,7 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
         a.token_of_slot = tos;
         a.v41 = mode.v41;
         a.lim = mode.lim;
+        a.ptr_table = mode.tables;
         a.pair_of_slot = pos;
         a.pair_w = topk_w;
         if (tiled) {
@@ -298,6 +325,7 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
         mx::SkinnyArgs a = {};
         a.w0 = static_cast<const uint8_t *>(down);
         a.expert_stride = tbytes;
+        a.ptr_table = mode.tables;
         a.rows = (int)hidden;
         a.cols = (int)inter;
         a.x = h_in ? h_in : h;
@@ -542,6 +570,50 @@ int moe_experts_mxfp4(const void *gate, const void *up, const void *down, int64_
                   topk_w, top_k, out, out_dtype, true, workspace, workspace_bytes));
     return moe_run(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
                    topk_w, top_k, out, out_dtype, workspace, nullptr, nullptr, MoeMode{},
+                   (hipStream_t)stream);
+}
+
+int mxfp4_device_address(const void *p, void **device_ptr)
+{
+    clear_error();
+    if (!p || !device_ptr)
+        return fail(MXFP4_EINVAL, "device_address: null pointer");
+    *device_ptr = nullptr;
+    hipPointerAttribute_t attr;
+    const hipError_t st = hipPointerGetAttributes(&attr, p);
+    if (st != hipSuccess) {
+        (void)hipGetLastError(); // the query's error is not a launch error
+        return fail(MXFP4_EINVAL, "%p is neither device memory nor pinned host memory (%s)", p,
+                    hipGetErrorString(st));
+    }
+    if (attr.type == hipMemoryTypeDevice) {
+        *device_ptr = const_cast<void *>(p);
+        return MXFP4_OK;
+    }
+    if (attr.type == hipMemoryTypeHost && attr.devicePointer) {
+        // the mapped address of the pinned block, at p's offset within it
+        const uintptr_t off =
+            reinterpret_cast<uintptr_t>(p) - reinterpret_cast<uintptr_t>(attr.hostPointer);
+        *device_ptr = static_cast<uint8_t *>(attr.devicePointer) + (attr.hostPointer ? off : 0);
+        return MXFP4_OK;
+    }
+    return fail(MXFP4_EINVAL, "%p is not device-accessible (memory type %d)", p, (int)attr.type);
+}
+
+int moe_experts_mxfp4_ptrs(const void *const *gate, const void *const *up,
+                           const void *const *down, int64_t n_experts, int64_t hidden,
+                           int64_t inter, const void *x, int x_dtype, int64_t n_tokens,
+                           const int32_t *topk_ids, const float *topk_w, int64_t top_k,
+                           void *out, int out_dtype, void *workspace, size_t workspace_bytes,
+                           void *stream)
+{
+    clear_error();
+    TRY(check_moe(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
+                  topk_w, top_k, out, out_dtype, true, workspace, workspace_bytes, true));
+    MoeMode mode = {};
+    mode.tables = true;
+    return moe_run(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
+                   topk_w, top_k, out, out_dtype, workspace, nullptr, nullptr, mode,
                    (hipStream_t)stream);
 }
 

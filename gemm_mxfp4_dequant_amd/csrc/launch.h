@@ -32,12 +32,16 @@ struct SkinnyArgs {
     float lim;
     const int *pair_of_slot;
     const float *pair_w;
+    // MoE: w0 / w1 are tables of per-expert tensor pointers (device arrays
+    // of n_experts pointers; an entry may point to device memory or to
+    // device-mapped pinned host memory) instead of contiguous banks.
+    int ptr_table;
     // Pads the struct to 128 bytes, so the hidden launch arguments the
     // compiler appends (grid and workgroup sizes) start at offset 128.
     // Measured against the unpadded 120 bytes, same code otherwise: 4096 x
     // 4096 matvec 5.04 -> 4.85 us, b = 8 6.97 -> 6.77 us, 64-expert decode
     // -0.4 %, 14336 x 4096 b = 8 +0.9 %.
-    int reserved_[2];
+    int reserved_;
 };
 static_assert(sizeof(SkinnyArgs) == 128, "SkinnyArgs layout: see reserved_");
 

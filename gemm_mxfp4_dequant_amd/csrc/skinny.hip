@@ -198,8 +198,9 @@ __device__ __forceinline__ void store_tile(const SkinnyArgs &a, const TileMap &t
 
 } // namespace
 
-// Split-K kernel: cols % KW == 0.  blockDim = nwr * (cols / KW) * 64.
-template <int KW, int TPC, bool XBF, int MODE, int MAXW>
+// Split-K kernel: cols % KW == 0.  blockDim = nwr * (cols / KW) * 64.  PT:
+// the banks are per-expert pointer tables.
+template <int KW, int TPC, bool XBF, int MODE, int MAXW, bool PT>
 __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
 {
     constexpr int LS = KW / 128; // load steps per wave
@@ -250,8 +251,10 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
     const int mat = wr / NR, tile = wr % NR;
     const int li = lane & 15, ls = lane >> 4;
     const int R = a.rows;
-    const uint8_t *A0 = a.w0 + (int64_t)tm.expert * a.expert_stride;
-    const uint8_t *A1 = (MODE == MODE_GATEUP) ? a.w1 + (int64_t)tm.expert * a.expert_stride : A0;
+    const uint8_t *A0 =
+        MODE == MODE_GEMM ? a.w0 : expert_base<PT>(a.w0, tm.expert, a.expert_stride);
+    const uint8_t *A1 =
+        (MODE == MODE_GATEUP) ? expert_base<PT>(a.w1, tm.expert, a.expert_stride) : A0;
     const int64_t code_bytes = (int64_t)R * (C / 2);
 
     // ---- 1.-2. activation, scale and weight loads.  The activations and
@@ -470,8 +473,12 @@ __global__ __launch_bounds__(NW * 64) void skinny_generic(SkinnyArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, ls = lane >> 4;
     const int R = a.rows;
-    const uint8_t *A0 = a.w0 + (int64_t)tm.expert * a.expert_stride;
-    const uint8_t *A1 = (MODE == MODE_GATEUP) ? a.w1 + (int64_t)tm.expert * a.expert_stride : A0;
+    const uint8_t *A0 = MODE == MODE_GEMM
+                            ? a.w0
+                            : expert_base_rt(a.w0, a.ptr_table, tm.expert, a.expert_stride);
+    const uint8_t *A1 = (MODE == MODE_GATEUP)
+                            ? expert_base_rt(a.w1, a.ptr_table, tm.expert, a.expert_stride)
+                            : A0;
     const int64_t code_bytes = (int64_t)R * (C / 2);
 
     // activations -> LDS (zero beyond C up to cpad)
@@ -576,33 +583,39 @@ constexpr int RB_MIN_WGS = 1024;
 typedef void (*KernelFn)(SkinnyArgs);
 
 struct Entry {
-    int mode, xbf, kw, tpc, maxw; // kw 0 = generic
+    int mode, xbf, kw, tpc, maxw, pt; // kw 0 = generic (either kind of bank)
     KernelFn fn;
 };
 
-#define MX_K(MODE, XBF, KW, TPC, MAXW) \
-    {MODE, XBF, KW, TPC, MAXW, skinny_splitk<KW, TPC, (bool)XBF, MODE, MAXW>}
-#define MX_KW(MODE, XBF, KW, TPC) MX_K(MODE, XBF, KW, TPC, 8), MX_K(MODE, XBF, KW, TPC, 16)
-#define MX_F32(MODE, KW) \
-    MX_KW(MODE, 0, KW, 1), MX_KW(MODE, 0, KW, 2), MX_KW(MODE, 0, KW, 4), MX_KW(MODE, 0, KW, 8)
-#define MX_B16(MODE, KW) \
-    MX_KW(MODE, 1, KW, 2), MX_KW(MODE, 1, KW, 4), MX_KW(MODE, 1, KW, 8), MX_KW(MODE, 1, KW, 16)
+#define MX_K(MODE, XBF, KW, TPC, MAXW, PT) \
+    {MODE, XBF, KW, TPC, MAXW, PT, skinny_splitk<KW, TPC, (bool)XBF, MODE, MAXW, (bool)PT>}
+#define MX_KW(MODE, XBF, KW, TPC, PT) \
+    MX_K(MODE, XBF, KW, TPC, 8, PT), MX_K(MODE, XBF, KW, TPC, 16, PT)
+#define MX_F32(MODE, KW, PT) \
+    MX_KW(MODE, 0, KW, 1, PT), MX_KW(MODE, 0, KW, 2, PT), MX_KW(MODE, 0, KW, 4, PT), \
+        MX_KW(MODE, 0, KW, 8, PT)
+#define MX_B16(MODE, KW, PT) \
+    MX_KW(MODE, 1, KW, 2, PT), MX_KW(MODE, 1, KW, 4, PT), MX_KW(MODE, 1, KW, 8, PT), \
+        MX_KW(MODE, 1, KW, 16, PT)
 #define MX_G(MODE, XBF, TPC) \
-    {MODE, XBF, 0, TPC, NW_GENERIC, skinny_generic<NW_GENERIC, TPC, (bool)XBF, MODE>}
+    {MODE, XBF, 0, TPC, NW_GENERIC, 0, skinny_generic<NW_GENERIC, TPC, (bool)XBF, MODE>}
 #define MX_GEN(MODE) \
     MX_G(MODE, 0, 1), MX_G(MODE, 0, 2), MX_G(MODE, 0, 4), MX_G(MODE, 0, 8), MX_G(MODE, 1, 2), \
         MX_G(MODE, 1, 4), MX_G(MODE, 1, 8), MX_G(MODE, 1, 16)
-#define MX_MODE(MODE) \
-    MX_F32(MODE, 512), MX_F32(MODE, 1024), MX_B16(MODE, 512), MX_B16(MODE, 1024), MX_GEN(MODE)
+#define MX_SPLITK(MODE, PT) \
+    MX_F32(MODE, 512, PT), MX_F32(MODE, 1024, PT), MX_B16(MODE, 512, PT), MX_B16(MODE, 1024, PT)
+#define MX_MODE(MODE) MX_SPLITK(MODE, 0), MX_GEN(MODE)
+// expert-bank modes also over per-expert pointer tables
+#define MX_MODE_BANK(MODE) MX_SPLITK(MODE, 0), MX_SPLITK(MODE, 1), MX_GEN(MODE)
 
-const Entry kTable[] = {MX_MODE(MODE_GEMM), MX_MODE(MODE_GATEUP), MX_MODE(MODE_DOWN)};
+const Entry kTable[] = {MX_MODE(MODE_GEMM), MX_MODE_BANK(MODE_GATEUP), MX_MODE_BANK(MODE_DOWN)};
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
-const Entry *find(int mode, bool xbf, int kw, int tpc, int maxw)
+const Entry *find(int mode, bool xbf, int kw, int tpc, int maxw, bool pt = false)
 {
     for (const Entry &e : kTable)
         if (e.mode == mode && e.xbf == (int)xbf && e.kw == kw && e.tpc == tpc &&
-            (kw == 0 || e.maxw == maxw))
+            (kw == 0 || (e.maxw == maxw && e.pt == (int)pt)))
             return &e;
     return nullptr;
 }
@@ -793,7 +806,7 @@ hipError_t skinny_launch(int mode, bool xbf, const SkinnyShape &s, SkinnyArgs a,
     a.rbw = s.kw ? s.rbw : 1;
     const unsigned blocks = (unsigned)skinny_blocks(s, a.rows, a.nch);
     const int waves = s.threads / 64;
-    const Entry *e = find(mode, xbf, s.kw, s.tpc, waves <= 8 ? 8 : 16);
+    const Entry *e = find(mode, xbf, s.kw, s.tpc, waves <= 8 ? 8 : 16, a.ptr_table != 0);
     if (!e)
         return hipErrorInvalidValue;
     // Opt in to more than 64 KB of LDS once per kernel, so that later

@@ -96,7 +96,7 @@ __device__ __forceinline__ void raw_barrier()
 
 } // namespace
 
-template <int NW, int RT, int NC, bool XBF, int MODE>
+template <int NW, int RT, int NC, bool XBF, int MODE, bool PT>
 __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
 {
     constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
@@ -178,7 +178,8 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     const uint8_t *Am[NMAT];
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat)
-        Am[mat] = (mat ? a.w1 : a.w0) + (int64_t)expert * a.expert_stride;
+        Am[mat] = MODE == MODE_GEMM ? a.w0
+                                    : expert_base<PT>(mat ? a.w1 : a.w0, expert, a.expert_stride);
 
     // ---- per-lane load sources (rows past the end read row R-1: never
     // stored, and MFMA output rows depend on their own A row only)
@@ -407,25 +408,29 @@ namespace {
 typedef void (*TiledFn)(SkinnyArgs);
 
 struct TEntry {
-    int mode, xbf, nw, rt, nc;
+    int mode, xbf, nw, rt, nc, pt;
     TiledFn fn;
 };
 
-#define MX_T(MODE, XBF, NW, RT, NC) \
-    {MODE, XBF, NW, RT, NC, tiled_kernel<NW, RT, NC, (bool)XBF, MODE>}
-#define MX_TX(MODE, NW, RT, NC) MX_T(MODE, 0, NW, RT, NC), MX_T(MODE, 1, NW, RT, NC)
+#define MX_T(MODE, XBF, NW, RT, NC, PT) \
+    {MODE, XBF, NW, RT, NC, PT, tiled_kernel<NW, RT, NC, (bool)XBF, MODE, (bool)PT>}
+#define MX_TX(MODE, NW, RT, NC) MX_T(MODE, 0, NW, RT, NC, 0), MX_T(MODE, 1, NW, RT, NC, 0)
+// expert-bank modes also over per-expert pointer tables
+#define MX_TXB(MODE, NW, RT, NC) \
+    MX_TX(MODE, NW, RT, NC), MX_T(MODE, 0, NW, RT, NC, 1), MX_T(MODE, 1, NW, RT, NC, 1)
 // expert bank: gate/up 8 waves x 1 row tile (four 32 KB stages), down 8 x 2
 // (one activation slab serves 256 rows: 1.67 -> 1.59 ms on the prefill bank);
 // GEMM: 4 waves x 1 row tile (more workgroups on 14336-row weights)
 const TEntry kTiled[] = {
-    MX_TX(MODE_GATEUP, 8, 1, 4), MX_TX(MODE_DOWN, 8, 2, 4),
+    MX_TXB(MODE_GATEUP, 8, 1, 4), MX_TXB(MODE_DOWN, 8, 2, 4),
     MX_TX(MODE_GEMM, 4, 1, 4), MX_TX(MODE_GEMM, 4, 1, 2),
 };
 
-const TEntry *tfind(int mode, bool xbf, int nw, int rt, int nc)
+const TEntry *tfind(int mode, bool xbf, int nw, int rt, int nc, bool pt)
 {
     for (const TEntry &e : kTiled)
-        if (e.mode == mode && e.xbf == (int)xbf && e.nw == nw && e.rt == rt && e.nc == nc)
+        if (e.mode == mode && e.xbf == (int)xbf && e.nw == nw && e.rt == rt && e.nc == nc &&
+            e.pt == (int)pt)
             return &e;
     return nullptr;
 }
@@ -441,7 +446,7 @@ int tiled_rows_per_wg(int nw, int rt) { return nw * rt * 16; }
 hipError_t tiled_launch(int mode, bool xbf, int nw, int rt, int nc, const SkinnyArgs &a,
                         hipStream_t stream)
 {
-    const TEntry *e = tfind(mode, xbf, nw, rt, nc);
+    const TEntry *e = tfind(mode, xbf, nw, rt, nc, a.ptr_table != 0);
     if (!e)
         return hipErrorInvalidValue;
     const int rpw = tiled_rows_per_wg(nw, rt);

@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
                                          P, ctypes.c_size_t, P, P, P]),
         "moe_experts_mxfp4_noalloc": (I, [P, P, P, I64, I64, I64, P, I, I64, P, P, I64, P, I,
                                           P]),
+        "moe_experts_mxfp4_ptrs": (I, [P, P, P, I64, I64, I64, P, I, I64, P, P, I64, P, I, P,
+                                       ctypes.c_size_t, P]),
+        "mxfp4_device_address": (I, [P, ctypes.POINTER(ctypes.c_void_p)]),
         "moe_experts_mxfp4_v41_workspace_size": (ctypes.c_size_t, [I64, I64, I64, I64, I64, I]),
         "moe_experts_mxfp4_v41": (I, [P, P, P, I64, I64, I64, P, I64, P, P, I64,
                                       ctypes.c_float, I, P, P, ctypes.c_size_t, P]),
@@ -308,6 +311,66 @@ def moe_experts_mxfp4(gate, up, down, n_experts, hidden, inter, x, topk_ids, top
     _check(lib().moe_experts_mxfp4(_ptr(gate), _ptr(up), _ptr(down), n_experts, hidden, inter,
                                    _ptr(x), _dt(x), T, _ptr(topk_ids), _ptr(topk_w), K, _ptr(out),
                                    _dt(out), _ptr(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+def mxfp4_device_address(t) -> int:
+    """Address kernels use for tensor ``t``'s data: a device tensor's own
+    pointer, or the mapped address of a pinned host tensor.  Raises for
+    pageable host memory."""
+    out = ctypes.c_void_p()
+    _check(lib().mxfp4_device_address(t.data_ptr(), ctypes.byref(out)))
+    return int(out.value)
+
+
+def expert_table(tensors, rows, cols, device=None):
+    """Device table of per-expert tensor addresses for moe_experts_mxfp4_ptrs
+    from a list of uint8 tensors, each either on the current device or in
+    pinned host memory (``torch.empty(..., pin_memory=True)``)."""
+    nb = _tensor_bytes(rows, cols)
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    addrs = []
+    for i, t in enumerate(tensors):
+        name = f"expert {i}"
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name}: expected a torch.Tensor")
+        if t.device.type == "cuda":
+            _req(t, name, _U8, nb, dev)
+        elif t.device.type == "cpu":
+            if not t.is_pinned():
+                raise ValueError(f"{name}: a host tensor must be in pinned memory")
+            if not t.is_contiguous() or t.dtype != torch.uint8 or t.numel() < nb:
+                raise ValueError(f"{name}: expected a contiguous uint8 tensor of {nb} bytes")
+        else:
+            raise ValueError(f"{name}: on {t.device}")
+        a = mxfp4_device_address(t)
+        if a % 16:
+            raise ValueError(f"{name}: data not 16-byte aligned")
+        addrs.append(a)
+    return torch.tensor(addrs, dtype=torch.int64, device=dev)
+
+
+def moe_experts_mxfp4_ptrs(gate_table, up_table, down_table, n_experts, hidden, inter, x,
+                           topk_ids, topk_w, out=None, out_dtype=torch.bfloat16, workspace=None,
+                           stream=None):
+    """The expert bank over per-expert pointer tables (``expert_table``):
+    each expert's tensors in device memory or pinned host memory."""
+    _sizes(n_experts=n_experts, hidden=hidden, inter=inter)
+    d = _req(gate_table, "gate_table", (torch.int64,), n_experts)
+    _req(up_table, "up_table", (torch.int64,), n_experts, d)
+    _req(down_table, "down_table", (torch.int64,), n_experts, d)
+    _req_current(d)
+    T, K, _ = _routing(topk_ids, d, topk_w)
+    _req(x, "x", _ACT, T * hidden, d)
+    if out is None:
+        out = torch.empty((T, hidden), dtype=out_dtype, device=d)
+    _req(out, "out", _ACT, T * hidden, d)
+    ws, ws_bytes = _ws(workspace, moe_experts_mxfp4_workspace_size(T, K, n_experts, hidden,
+                                                                   inter, _dt(x)), d)
+    _check(lib().moe_experts_mxfp4_ptrs(_ptr(gate_table), _ptr(up_table), _ptr(down_table),
+                                        n_experts, hidden, inter, _ptr(x), _dt(x), T,
+                                        _ptr(topk_ids), _ptr(topk_w), K, _ptr(out), _dt(out),
+                                        _ptr(ws), ws_bytes, _stream(stream)))
     return out
 
 

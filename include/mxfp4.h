@@ -155,6 +155,36 @@ int moe_experts_mxfp4(const void *gate, const void *up, const void *down, int64_
                       const int32_t *topk_ids, const float *topk_w, int64_t top_k, void *out,
                       int out_dtype, void *workspace, size_t workspace_bytes, void *stream);
 
+/* moe_experts_mxfp4 with each expert's tensors anywhere the GPU can read:
+ * gate, up and down are tables of n_experts pointers (device arrays, 8-byte
+ * aligned), entry e pointing to expert e's tensor (16-byte aligned, the
+ * stored two-plane layout) in device memory or in pinned host memory mapped
+ * into the device address space (hipHostMalloc).  This serves the experts a
+ * card's memory does not hold ("cortiq-engine 0.8.77, src/qtensor/
+ * moe_fast.rs", module contract; "cortiq-engine 0.8.40,
+ * src/gpu_wgpu/mxfp4.rs", global_bank_case's cold winner): the same kernels
+ * read a host-resident expert's weights over the host link, once per work
+ * item, with no copy into device memory and no CPU arithmetic.  Results
+ * equal moe_experts_mxfp4's on the same weights bit for bit.  The table
+ * entries are device data and are not checked: each must be a valid,
+ * device-accessible pointer to a tensor of the stated shape.  Other
+ * arguments, workspace and errors as moe_experts_mxfp4 (workspace size from
+ * moe_experts_mxfp4_workspace_size). */
+int moe_experts_mxfp4_ptrs(const void *const *gate, const void *const *up,
+                           const void *const *down, int64_t n_experts, int64_t hidden,
+                           int64_t inter, const void *x, int x_dtype, int64_t n_tokens,
+                           const int32_t *topk_ids, const float *topk_w, int64_t top_k,
+                           void *out, int out_dtype, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* The address at which kernels on the current device read the memory at p:
+ * p itself for device memory, the mapped address for pinned host memory
+ * (hipHostMalloc).  Host only (a runtime query, no allocation).  Returns
+ * MXFP4_EINVAL for pageable host memory or any pointer the runtime does not
+ * know, which no kernel may be given.  For building the tables of
+ * moe_experts_mxfp4_ptrs. */
+int mxfp4_device_address(const void *p, void **device_ptr);
+
 /* moe_experts_mxfp4 for callers that cannot allocate (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * computation and result, bit for bit, with no workspace argument and no
