@@ -60,6 +60,12 @@ def _load():
     lib.orc_bf16_rne.argtypes = [ctypes.c_double]
     lib.orc_bf16_rne_n.restype = None
     lib.orc_bf16_rne_n.argtypes = [P, I64, P]
+    lib.orc_e4m3.restype = ctypes.c_double
+    lib.orc_e4m3.argtypes = [ctypes.c_int]
+    lib.orc_e4m3_rne.restype = ctypes.c_int
+    lib.orc_e4m3_rne.argtypes = [ctypes.c_double]
+    lib.orc_mxfp8_quantize.restype = None
+    lib.orc_mxfp8_quantize.argtypes = [P, I64, I64, P, P]
     lib.orc_gemm.restype = None
     lib.orc_gemm.argtypes = [P, I64, I64, P, I64, P, P, ctypes.c_int]
     lib.orc_gemm_rows.restype = None
@@ -167,6 +173,52 @@ def bf16_rne_array(a) -> np.ndarray:
 def bf16_bits_to_f64(bits) -> np.ndarray:
     bits = np.asarray(bits, dtype=np.uint16)
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# MXFP8 activations (the opt-in block-scaled FP4 x FP8 product)
+# --------------------------------------------------------------------------
+
+def e4m3(code: int) -> float:
+    """Value of an E4M3 code.  Pinned by test_oracle_mx8."""
+    return _load().orc_e4m3(int(code))
+
+
+def e4m3_rne(v: float) -> int:
+    """Nearest E4M3 code (ties to even, saturating).  Pinned by
+    test_oracle_mx8."""
+    return int(_load().orc_e4m3_rne(float(v)))
+
+
+def mxfp8_quantize(x):
+    """MXFP8 quantization of activations [b, cols] (cols % 32 == 0):
+    E4M3 codes uint8 [b, cols] and E8M0 scale bytes uint8 [b, cols/32].
+    Pinned by test_oracle_mx8."""
+    x = _as_f64(x)
+    b, cols = x.shape
+    assert cols % 32 == 0
+    q = np.empty((b, cols), np.uint8)
+    s = np.empty((b, cols // 32), np.uint8)
+    _load().orc_mxfp8_quantize(_ptr(x), b, cols, _ptr(q), _ptr(s))
+    return q, s
+
+
+def mxfp8_dequantize(q, s) -> np.ndarray:
+    """fp64 values of MXFP8 activations: e4m3(q) * 2^(s - 127) (NaN for a
+    scale byte of 255)."""
+    q = np.asarray(q, np.uint8)
+    s = np.asarray(s, np.uint8)
+    tab = np.array([e4m3(c) for c in range(256)], np.float64)
+    sc = np.where(s == 255, np.nan, np.ldexp(1.0, s.astype(np.int64) - 127))
+    return tab[q] * np.repeat(sc, 32, axis=1)
+
+
+def gemm_a8(w, rows: int, cols: int, x, threads: int | None = None):
+    """The block-scaled FP4 x FP8 product: the exact product (``gemm``) of
+    the weights with the MXFP8-quantized activations.  Returns
+    (y [b, rows] fp64, mag = sum |w * x_q|)."""
+    q, s = mxfp8_quantize(x)
+    return gemm(w, rows, cols, mxfp8_dequantize(q, s), threads)
 
 
 # --------------------------------------------------------------------------

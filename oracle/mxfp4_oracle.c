@@ -186,6 +186,98 @@ void orc_dequant_bf16(const uint8_t *w, int64_t rows, int64_t cols, uint16_t *ou
 }
 
 /* ------------------------------------------------------------------------ */
+/* MXFP8 activations: the activation side of the block-scaled FP4 x FP8     */
+/* product.  [wgpu] module doc: the OCP MX family (a shared E8M0 power-of-  */
+/* two scale per 32 elements); here with E4M3 elements, as that family      */
+/* defines them.                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* E4M3 element: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits
+ * 2..0; exponent field 0 is subnormal, m * 2^-9; S.1111.111 is NaN; there
+ * are no infinities; the largest finite magnitude is 1.75 * 2^8 = 448.
+ * Pinned by test_oracle_mx8.py (all 256 codes against the field
+ * definition). */
+double orc_e4m3(int code)
+{
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+/* The E4M3 code nearest to v: the finite magnitude closest to |v| by exact
+ * search over the 127 non-negative finite codes, a tie going to the code
+ * with an even mantissa; magnitudes beyond 448 therefore saturate to 448;
+ * the sign is kept (-0 for negative values that round to zero); NaN gives
+ * 0x7F.  Pinned by test_oracle_mx8.py. */
+int orc_e4m3_rne(double v)
+{
+    if (isnan(v))
+        return 0x7F;
+    int sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a >= 448.0) /* the largest finite magnitude is the nearest */
+        return sign | 0x7E;
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c < 0x7F; ++c) {
+        double d = fabs(a - orc_e4m3(c));
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return sign | best;
+}
+
+/* MXFP8 quantization of x [rows][cols] (cols % 32 == 0) into E4M3 codes
+ * q [rows][cols] and E8M0 scale bytes s [rows][cols/32], block by block of
+ * 32 elements of a row: with a = the largest magnitude of the block, the
+ * shared exponent is E = floor(log2 a) - 8 (8: the exponent of E4M3's
+ * largest binade), stored as the byte E + 127 clamped to [0, 254]; each
+ * element is the E4M3 code nearest to v / 2^E.  The block's largest then
+ * lies in [256, 512) and saturates to 448 when above it (up to 1/8 of its
+ * magnitude), as the MX conversion rule has it.  A block whose largest
+ * magnitude is 0 takes the byte 0 (2^-127) and zero codes; a block holding
+ * NaN or an infinity takes 255 (NaN) and zero codes.  Pinned by
+ * test_oracle_mx8.py. */
+void orc_mxfp8_quantize(const double *x, int64_t rows, int64_t cols, uint8_t *q, uint8_t *s)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t g = 0; g < cols / 32; ++g) {
+            const double *v = x + r * cols + g * 32;
+            uint8_t *qq = q + r * cols + g * 32;
+            double a = 0.0;
+            int bad = 0;
+            for (int i = 0; i < 32; ++i) {
+                if (!isfinite(v[i]))
+                    bad = 1;
+                else if (fabs(v[i]) > a)
+                    a = fabs(v[i]);
+            }
+            if (bad || a == 0.0) {
+                s[r * (cols / 32) + g] = bad ? 255 : 0;
+                for (int i = 0; i < 32; ++i)
+                    qq[i] = 0;
+                continue;
+            }
+            int e2;
+            frexp(a, &e2);       /* a = f * 2^e2, f in [0.5, 1): floor(log2 a) = e2 - 1 */
+            int E = (e2 - 1) - 8;
+            int k = E + 127;
+            if (k < 0)
+                k = 0;
+            if (k > 254)
+                k = 254;
+            E = k - 127;
+            s[r * (cols / 32) + g] = (uint8_t)k;
+            for (int i = 0; i < 32; ++i)
+                qq[i] = (uint8_t)orc_e4m3_rne(ldexp(v[i], -E));
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dense product: y[t][r] = sum_c W[r][c] * x[t][c], mag = sum |W x|         */
 /* ------------------------------------------------------------------------ */
 
