@@ -447,6 +447,26 @@ def main():
             extra[f"gemm_14336x4096_b{b}"] = gemm_line(s, ms, t, ceil_3)
             log(f"gemm_14336x4096_b{b}: {extra[f'gemm_14336x4096_b{b}']}")
             del s, t
+        # the opt-in block-scaled FP4 x FP8 product (activations quantized to
+        # MXFP8 in the call; its own accuracy contract) beside the exact path,
+        # at 64 tokens
+        for xname, xdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+            rows_, cols_, b = 14336, 4096, 64
+            s = gemm_setup(torch, mx, inputs, rows_, cols_, b, 90)
+            x = s["x"].to(xdt)
+            ws = torch.empty(mx.mxfp4_gemm_a8_workspace_size(b, cols_), dtype=torch.uint8,
+                             device="cuda")
+            for name, fn in (("a8", lambda i: mx.mxfp4_gemm_a8(s["pool"][i], rows_, cols_, x,
+                                                               b=b, y=s["y"], workspace=ws)),
+                             ("exact", lambda i: mx.mxfp4_gemm(s["pool"][i], rows_, cols_, x,
+                                                               b=b, y=s["y"]))):
+                t = Timer(torch, [lambda i=i: fn(i) for i in range(s["n"])], args.eager)
+                ms = t.time(max(3, 1000 // s["n"]))
+                key = f"gemm_{name}_14336x4096_b64_{xname}"
+                extra[key] = gemm_line(s, ms, t, ceil_3)
+                log(f"{key}: {extra[key]}")
+                del t
+            del s, ws, x
         torch.cuda.empty_cache()
     if "decode" in sections:
         # expert bank, decode layer (2 banks alternate: 466 MB touched per step)

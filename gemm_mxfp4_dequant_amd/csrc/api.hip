@@ -494,6 +494,70 @@ int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_d
     return launched(mx::skinny_launch(mx::MODE_GEMM, xbf, sh, a, (hipStream_t)stream), "gemm");
 }
 
+size_t mxfp4_gemm_a8_workspace_size(int64_t b, int64_t cols)
+{
+    if (b < 1 || b > MXFP4_MAX_TOKENS || cols < 128 || cols > MXFP4_MAX_COLS || cols % 128)
+        return 0;
+    return align256((size_t)b * cols) + align256((size_t)b * (cols / 32));
+}
+
+int mxfp8_quantize(const void *x, int x_dtype, int64_t b, int64_t cols, uint8_t *q, uint8_t *s,
+                   void *stream)
+{
+    clear_error();
+    TRY(check_dtype("x_dtype", x_dtype));
+    if (b < 1 || b > MXFP4_MAX_TOKENS)
+        return fail(MXFP4_EINVAL, "b = %lld outside [1, %d]", (long long)b, MXFP4_MAX_TOKENS);
+    if (cols < 32 || cols > MXFP4_MAX_COLS || cols % 32)
+        return fail(MXFP4_EINVAL, "cols = %lld must be a multiple of 32 in [32, %d]",
+                    (long long)cols, MXFP4_MAX_COLS);
+    TRY(check_buffer("x", x, 16));
+    TRY(check_buffer("q", q, 16));
+    TRY(check_buffer("s", s, 1));
+    return launched(mx::mxfp8_quantize_launch(x, x_dtype == MXFP4_BF16, b, cols, q, s,
+                                              (hipStream_t)stream),
+                    "mxfp8 quantize");
+}
+
+int mxfp4_gemm_a8(const void *w, int64_t rows, int64_t cols, const void *x, int x_dtype,
+                  int64_t b, void *y, int y_dtype, void *workspace, size_t workspace_bytes,
+                  void *stream)
+{
+    clear_error();
+    TRY(check_tensor("w", w, rows, cols));
+    if (cols % 128)
+        return fail(MXFP4_EINVAL, "cols = %lld: the FP4 x FP8 product needs a multiple of 128",
+                    (long long)cols);
+    TRY(check_dtype("x_dtype", x_dtype));
+    TRY(check_dtype("y_dtype", y_dtype));
+    if (b < 1 || b > MXFP4_MAX_TOKENS)
+        return fail(MXFP4_EINVAL, "b = %lld outside [1, %d]", (long long)b, MXFP4_MAX_TOKENS);
+    TRY(check_buffer("x", x, 16));
+    TRY(check_buffer("y", y, 16));
+    TRY(check_buffer("workspace", workspace, 16));
+    const size_t need = mxfp4_gemm_a8_workspace_size(b, cols);
+    if (workspace_bytes < need)
+        return fail(MXFP4_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    const int64_t nrb = (rows + mx::a8_rows_per_wg() - 1) / mx::a8_rows_per_wg();
+    if (nrb * ((b + 15) / 16) > ((int64_t)1 << 31) - 1)
+        return fail(MXFP4_EINVAL, "rows * b too large for one launch");
+    uint8_t *q = static_cast<uint8_t *>(workspace);
+    uint8_t *sc = q + align256((size_t)b * cols);
+    const hipStream_t st = (hipStream_t)stream;
+    TRY(launched(mx::mxfp8_quantize_launch(x, x_dtype == MXFP4_BF16, b, cols, q, sc, st),
+                 "mxfp8 quantize"));
+    mx::A8Args a = {};
+    a.w = static_cast<const uint8_t *>(w);
+    a.rows = (int)rows;
+    a.cols = (int)cols;
+    a.xq = q;
+    a.xs = sc;
+    a.b = (int)b;
+    a.y = y;
+    a.y_bf16 = y_dtype == MXFP4_BF16;
+    return launched(mx::gemm_a8_launch(a, st), "gemm a8");
+}
+
 int mxfp4_matvec(const void *w, int64_t rows, int64_t cols, const float *x, float *y, void *stream)
 {
     return mxfp4_gemm(w, rows, cols, x, MXFP4_F32, 1, y, MXFP4_F32, stream);

@@ -71,6 +71,22 @@ int tiled_rows_per_wg(int nw, int rt);
 hipError_t tiled_launch(int mode, bool xbf, int nw, int rt, int nc, const SkinnyArgs &a,
                         hipStream_t stream);
 
+// Block-scaled FP4 x FP8 product (mx8.hip): activations quantized to MXFP8
+// (E4M3 codes xq [b][cols], E8M0 scale bytes xs [b][cols / 32]), then
+// v_mfma_scale_f32_16x16x128_f8f6f4 with the weights as stored.
+struct A8Args {
+    const uint8_t *w;
+    int rows, cols; // cols % 128 == 0
+    const uint8_t *xq, *xs;
+    int b;
+    void *y; // [b][rows]
+    int y_bf16;
+};
+hipError_t mxfp8_quantize_launch(const void *x, bool xbf, int64_t b, int64_t cols, uint8_t *q,
+                                 uint8_t *s, hipStream_t stream);
+hipError_t gemm_a8_launch(const A8Args &a, hipStream_t stream);
+int a8_rows_per_wg();
+
 hipError_t dequant_launch(const uint8_t *w, int64_t rows, int64_t cols, void *out, bool bf16,
                           hipStream_t stream);
 

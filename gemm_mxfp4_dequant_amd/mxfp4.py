@@ -53,6 +53,9 @@ def lib() -> ctypes.CDLL:
         "mxfp4_dequant": (I, [P, I64, I64, P, I, P]),
         "mxfp4_matvec": (I, [P, I64, I64, P, P, P]),
         "mxfp4_gemm": (I, [P, I64, I64, P, I, I64, P, I, P]),
+        "mxfp8_quantize": (I, [P, I, I64, I64, P, P, P]),
+        "mxfp4_gemm_a8_workspace_size": (ctypes.c_size_t, [I64, I64]),
+        "mxfp4_gemm_a8": (I, [P, I64, I64, P, I, I64, P, I, P, ctypes.c_size_t, P]),
         "moe_route_group": (I, [P, I64, I64, I64, P, P, P, P]),
         "moe_route_topk": (I, [P, I64, I64, I64, P, P, P]),
         "moe_experts_mxfp4_workspace_size": (ctypes.c_size_t, [I64, I64, I64, I64, I64, I]),
@@ -209,6 +212,52 @@ def mxfp4_gemm(w, rows, cols, x, b=None, y=None, y_dtype=torch.float32, stream=N
     _req(y, "y", _ACT, b * rows, d)
     _check(lib().mxfp4_gemm(_ptr(w), rows, cols, _ptr(x), _dt(x), b, _ptr(y), _dt(y),
                             _stream(stream)))
+    return y
+
+
+def mxfp8_quantize(x, q=None, s=None, stream=None):
+    """MXFP8 quantization of activations x [b, cols]: E4M3 codes q uint8
+    [b, cols] and E8M0 scale bytes s uint8 [b, cols/32]."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x: expected a [b, cols] tensor")
+    d = _req(x, "x", _ACT)
+    _req_current(d)
+    b, cols = x.shape
+    if q is None:
+        q = torch.empty((b, cols), dtype=torch.uint8, device=d)
+    if s is None:
+        s = torch.empty((b, cols // 32), dtype=torch.uint8, device=d)
+    _req(q, "q", _U8, b * cols, d)
+    _req(s, "s", _U8, b * (cols // 32), d)
+    _check(lib().mxfp8_quantize(_ptr(x), _dt(x), b, cols, _ptr(q), _ptr(s), _stream(stream)))
+    return q, s
+
+
+def mxfp4_gemm_a8_workspace_size(b, cols) -> int:
+    return int(lib().mxfp4_gemm_a8_workspace_size(b, cols))
+
+
+def mxfp4_gemm_a8(w, rows, cols, x, b=None, y=None, y_dtype=torch.float32, workspace=None,
+                  stream=None):
+    """Opt-in block-scaled FP4 x FP8 GEMM (activations quantized to MXFP8;
+    its own accuracy contract, see include/mxfp4.h)."""
+    if b is None:
+        b = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() >= 1 else 0
+    _sizes(rows=rows, cols=cols, b=b)
+    d = _req(w, "w", _U8, _tensor_bytes(rows, cols))
+    _req_current(d)
+    _req(x, "x", _ACT, b * cols, d)
+    if y is None:
+        y = torch.empty((b, rows), dtype=y_dtype, device=d)
+    _req(y, "y", _ACT, b * rows, d)
+    need = mxfp4_gemm_a8_workspace_size(b, cols)
+    if need <= 0:
+        raise ValueError(f"b = {b}, cols = {cols}: no FP4 x FP8 product (cols % 128 != 0?)")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=d)
+    _req(workspace, "workspace", _U8, need, d)
+    _check(lib().mxfp4_gemm_a8(_ptr(w), rows, cols, _ptr(x), _dt(x), b, _ptr(y), _dt(y),
+                               _ptr(workspace), workspace.numel(), _stream(stream)))
     return y
 
 

@@ -93,6 +93,45 @@ int mxfp4_matvec(const void *w, int64_t rows, int64_t cols, const float *x, floa
 int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_dtype, int64_t b,
                void *y, int y_dtype, void *stream);
 
+/* MXFP8 quantization of activations, the activation side of
+ * mxfp4_gemm_a8 (the OCP MX family that "cortiq-engine 0.8.40,
+ * src/gpu_wgpu/mxfp4.rs" names in its module doc, with E4M3 elements):
+ * for each block of 32 consecutive elements of a row of x [b][cols]
+ * (x_dtype MXFP4_F32 or MXFP4_BF16, cols % 32 == 0), with a = the block's
+ * largest magnitude, the shared exponent E = floor(log2 a) - 8 is stored as
+ * the byte E + 127 clamped to [0, 254] in s [b][cols/32], and each element
+ * becomes the E4M3 code (sign bit 7, exponent bias 7, 3 mantissa bits,
+ * largest finite 448) nearest to x / 2^E, ties to even, magnitudes above
+ * 448 saturating to 448, in q [b][cols].  A block of zeros gives the byte 0
+ * and zero codes; a block holding NaN or an infinity gives 255 (NaN) and
+ * zero codes.  x, q 16-byte aligned. */
+int mxfp8_quantize(const void *x, int x_dtype, int64_t b, int64_t cols, uint8_t *q, uint8_t *s,
+                   void *stream);
+
+/* Workspace bytes of mxfp4_gemm_a8 (the quantized activations); 0 on bad
+ * sizes (cols must be a multiple of 128). */
+size_t mxfp4_gemm_a8_workspace_size(int64_t b, int64_t cols);
+
+/* Opt-in block-scaled FP4 x FP8 GEMM: y[t][r] = sum_c W[r][c] * xq[t][c],
+ * where xq is x quantized to MXFP8 (mxfp8_quantize), on the CDNA4
+ * block-scaled matrix instruction v_mfma_scale_f32_16x16x128_f8f6f4: the
+ * weights enter as stored (E2M1 codes with their E8M0 scales), the
+ * activations as E4M3 with theirs, no decode.  Accuracy (its own contract,
+ * not the 1e-4 rule of mxfp4_gemm): within 2^-7 * sum_c |W[r][c] *
+ * xq[t][c]| of the exact product with the quantized activations (the
+ * matrix core adds 32-element blocks exactly but aligns the products inside
+ * a block to the block's largest); against the unquantized x the MXFP8
+ * rounding adds up to 2^-4 of each element (1/8 for a block's largest when
+ * it saturates).  Worth it where a product is a dense contraction (tens of
+ * tokens and more).  cols % 128 == 0; x [b][cols] of x_dtype; y [b][rows]
+ * of y_dtype; workspace at least mxfp4_gemm_a8_workspace_size(b, cols)
+ * bytes, 16-byte aligned, scratch owned by the call until the stream
+ * reaches it.  Errors as mxfp4_gemm, MXFP4_EWORKSPACE for a short
+ * workspace. */
+int mxfp4_gemm_a8(const void *w, int64_t rows, int64_t cols, const void *x, int x_dtype,
+                  int64_t b, void *y, int y_dtype, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
 /* Stable grouping of routed pairs by expert (the first step of the expert
  * bank), exposed for callers and tests.  Pairs are p = t*top_k + k.
  *   offsets [n_experts+1]: pairs of expert e occupy slots

@@ -1,0 +1,187 @@
+"""The opt-in block-scaled FP4 x FP8 product (mxfp4_gemm_a8) and its MXFP8
+activation quantizer (mxfp8_quantize), through the C ABI.
+
+* quantizer: E4M3 codes and E8M0 scale bytes bit-exact against the oracle
+  (a quantized code is an integer decision), fp32 and bf16 activations,
+  with random blocks over a wide range and special blocks (zeros, NaN,
+  inf, saturating, flushed elements, ties, fp32 subnormals);
+* characterization of the matrix instruction's accumulation, on crafted
+  inputs whose quantization is exact (so the output is a known sum of
+  products): products in different 32-element blocks add exactly (1 +
+  2^-k for k up to 23); inside one block a product 2^-4 .. 2^-13 below the
+  block's largest adds exactly and one 2^-14 .. 2^-20 below is dropped;
+  the products are summed in groups of 8 columns, each aligned to its own
+  largest (small products sharing the largest's group are lost, whole
+  groups of them elsewhere are kept);
+* parity: every output within 2^-7 * sum |w * x_q| of the oracle's exact
+  product with the quantized activations (the entry point's contract,
+  derived from the characterization: at most 31 * 2^-13 of a block's
+  largest product is lost per block), on the 4096 x 4096 and 14336 x 4096
+  shapes and ragged ones, fp32 and bf16 in and out;
+* invariants: token permutation permutes the output bit for bit; reruns are
+  bitwise equal; a NaN weight scale gives a NaN row.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gemm_mxfp4_dequant_amd import inputs
+from tests.helpers import assert_within, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    from gemm_mxfp4_dequant_amd import mxfp4
+    mxfp4.lib()
+    return mxfp4
+
+
+def special_blocks(cols):
+    rows = []
+    z = np.zeros(cols, np.float32)
+    rows.append(z.copy())                                       # all zero
+    r = np.ones(cols, np.float32)
+    r[5] = np.nan
+    rows.append(r)                                              # NaN block
+    r = np.ones(cols, np.float32)
+    r[40] = np.inf
+    r[70] = -np.inf
+    rows.append(r)                                              # inf blocks
+    r = np.zeros(cols, np.float32)
+    r[0:32] = [500.0, 460.0, 449.0, 448.0] + [1.0] * 28        # saturation
+    r[32:64] = [1.0, 1.0625, 1.09375, -1.0625] + [2.0 ** -19] * 28   # ties, flush
+    r[64:96] = np.float32(1e-40)                                # fp32 subnormal block
+    r[96:128] = [3.0e38] + [-1.0] * 31                          # largest binade
+    rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_quantize_bit_exact(m, orc, xdt):
+    cols = 256
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((60, cols)) *
+         np.exp2(rng.integers(-40, 40, size=(60, cols // 32)).repeat(32, axis=1))).astype(np.float32)
+    x = np.concatenate([x, special_blocks(cols)])
+    if xdt == "bf16":
+        xb = inputs.to_bf16_bits(x)
+        xd = dev(xb)
+        x = (xb.astype(np.uint32) << 16).view(np.float32)
+    else:
+        xd = dev(x)
+    q, s = m.mxfp8_quantize(xd)
+    torch.cuda.synchronize()
+    qo, so = orc.mxfp8_quantize(x)
+    assert np.array_equal(host(s), so)
+    assert np.array_equal(host(q), qo)
+
+
+def crafted(m, rows_w, x, rows=16, cols=128):
+    """Run the product on crafted weights: rows_w maps (row, col) to
+    (code, scale byte of that group); every other code is 0 and every
+    other scale byte 127."""
+    nb = rows * cols // 2 + rows * cols // 32
+    w = np.zeros(nb, np.uint8)
+    w[rows * cols // 2:] = 127
+    for (r, c), (code, sc) in rows_w.items():
+        byte = r * cols // 2 + c // 2
+        w[byte] |= (code << 4) if c % 2 else code
+        w[rows * cols // 2 + r * (cols // 32) + c // 32] = sc
+    y = m.mxfp4_gemm_a8(dev(w), rows, cols, dev(np.asarray(x, np.float32)))
+    torch.cuda.synchronize()
+    return host(y)
+
+
+def test_blocks_add_exactly(m):
+    """Products in different 32-element blocks add exactly: 1 + 2^-k."""
+    for k in range(1, 24):
+        x = np.zeros((1, 128), np.float32)
+        x[0, 0] = 1.0
+        x[0, 32] = 1.0
+        # w[0][0] = 1 (code 2, scale 127); w[0][32] = 2^-k (code 2, scale 127 - k)
+        y = crafted(m, {(0, 0): (2, 127), (0, 32): (2, 127 - k)}, x)
+        assert y[0, 0] == np.float32(1.0 + 2.0 ** -k), (k, y[0, 0])
+        assert not y[0, 1:].any()
+
+
+def test_in_block_alignment(m):
+    """Inside one 32-element block the products are aligned to the block's
+    largest: a second product 2^-4 .. 2^-13 below it adds exactly, one
+    2^-14 .. 2^-20 below is dropped."""
+    for d in range(4, 21):
+        x = np.zeros((1, 128), np.float32)
+        x[0, 0] = 1.0
+        x[0, 1] = 2.0 ** -(d - 1)     # in the block of 1.0: exact in E4M3 for d <= 16
+        # w[0][0] = 1 (code 2), w[0][1] = 0.5 (code 1), one group scale
+        y = crafted(m, {(0, 0): (2, 127), (0, 1): (1, 127)}, x)
+        want = 1.0 + 2.0 ** -d if d <= 13 else 1.0
+        if d > 16:
+            # the activation itself flushes below 2^-9 of the block scale
+            want = 1.0
+        assert y[0, 0] == np.float32(want), (d, y[0, 0], want)
+
+
+def test_in_block_groups_of_eight(m):
+    """The 32 products of a block are summed in groups of 8 consecutive
+    columns, each group's small products aligned to the group's largest:
+    with the largest (1.0) at column 0 and products of 2^-14 at the other
+    31 columns, the 7 sharing its group are dropped and the other three
+    groups (8 x 2^-14 = 2^-11 each) are kept exactly.  The loss, 7 x 2^-14
+    of the largest, is inside the entry point's 2^-7 contract."""
+    cases = {tuple(range(1, 32)): 1.0 + 24 * 2.0 ** -14,   # three groups kept
+             tuple(range(8, 16)): 1.0 + 8 * 2.0 ** -14,    # one whole group kept
+             tuple(range(1, 8)): 1.0,                      # the largest's group: dropped
+             tuple(range(24, 32)): 1.0 + 8 * 2.0 ** -14}
+    for cols_small, want in cases.items():
+        x = np.zeros((1, 128), np.float32)
+        x[0, 0] = 1.0
+        x[0, list(cols_small)] = 2.0 ** -14
+        y = crafted(m, {(0, c): (2, 127) for c in range(32)}, x)
+        assert y[0, 0] == np.float32(want), (cols_small[0], y[0, 0], want)
+        exact = 1.0 + len(cols_small) * 2.0 ** -14
+        assert abs(y[0, 0] - exact) <= 2.0 ** -7 * exact
+
+
+def check(m, orc, rows, cols, b, seed, xdt="f32", y_dtype=torch.float32):
+    w, x = inputs.gemm_case(seed, rows, cols, b, 118, 132, xdt)
+    y = m.mxfp4_gemm_a8(dev(w), rows, cols, dev(x), y_dtype=y_dtype)
+    torch.cuda.synchronize()
+    y = host(y)
+    if y_dtype == torch.bfloat16:
+        y = (y.astype(np.uint32) << 16).view(np.float32)
+    xf = x if xdt == "f32" else (x.astype(np.uint32) << 16).view(np.float32)
+    want, mag = orc.gemm_a8(w, rows, cols, xf)
+    extra = 0.0
+    if y_dtype == torch.bfloat16:
+        extra = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 1e-38))) - 7)
+    assert_within(y, want, mag, rel=2.0 ** -7, extra=extra, what=f"a8 {rows}x{cols} b={b}")
+    return w, x, y
+
+
+@pytest.mark.parametrize("rows,cols,b", [(4096, 4096, 1), (4096, 4096, 16), (4096, 4096, 64),
+                                         (14336, 4096, 40), (70, 512, 3), (300, 2304, 17),
+                                         (1000, 128, 100), (12300, 1024, 64)])
+def test_parity_at_the_contract(m, orc, rows, cols, b):
+    check(m, orc, rows, cols, b, rows + cols + b)
+
+
+def test_bf16_in_and_out(m, orc):
+    check(m, orc, 2048, 4096, 33, 7, xdt="bf16", y_dtype=torch.bfloat16)
+
+
+def test_invariants(m):
+    rows, cols, b = 512, 2048, 48
+    w, x = inputs.gemm_case(9, rows, cols, b)
+    wd = dev(w)
+    y = host(m.mxfp4_gemm_a8(wd, rows, cols, dev(x)))
+    y2 = host(m.mxfp4_gemm_a8(wd, rows, cols, dev(x)))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    perm = np.random.default_rng(1).permutation(b)
+    yp = host(m.mxfp4_gemm_a8(wd, rows, cols, dev(x[perm])))
+    assert np.array_equal(yp.view(np.uint32), y[perm].view(np.uint32))
+    w = w.copy()
+    w[rows * cols // 2 + 17 * (cols // 32) + 3] = 255
+    yn = host(m.mxfp4_gemm_a8(dev(w), rows, cols, dev(x)))
+    assert np.all(np.isnan(yn[:, 17])) and not np.isnan(np.delete(yn, 17, axis=1)).any()
