@@ -9,9 +9,10 @@
 //
 // How (MI355X design, not the pages' workgroup-per-row shader):
 //  * A workgroup owns NR tiles of 16 output rows (per matrix) and all of K,
-//    for one or several consecutive row blocks (the tokens stay in LDS while
-//    it walks the blocks; the next block's weights are in flight while the
-//    current one computes).  Its waves form a grid: row tile x K slab.  A wave streams its 16 rows
+//    for one or several row blocks (consecutive in the plain GEMM, evenly
+//    spaced in the expert bank; the tokens stay in LDS while it walks the
+//    blocks; the next block's weights are in flight while the current one
+//    computes).  Its waves form a grid: row tile x K slab.  A wave streams its 16 rows
 //    over one slab of KW columns with 128-bit loads, a lane loading one
 //    whole 32-column group (16 bytes) of one row per load step; all of a
 //    wave's loads are issued before it waits for any of them.
@@ -58,10 +59,8 @@ struct TileMap {
     int expert; // MoE expert (0 for GEMM)
 };
 
-// Work item of this workgroup; false if it has none (MoE grids are sized by
-// an upper bound).  Flattened logical grid, item/chunk fastest, laid out so
-// that the chunks / work items of one row block run on one XCD: a row
-// block's weights are read from HBM once and re-read from that XCD's L2.
+// Work item `sub` of this workgroup; false if it has none (MoE grids are
+// sized by an upper bound).
 template <int MODE, int TPC>
 __device__ __forceinline__ bool item_map(const SkinnyArgs &a, int sub, TileMap &m)
 {
@@ -82,6 +81,9 @@ __device__ __forceinline__ bool item_map(const SkinnyArgs &a, int sub, TileMap &
     return true;
 }
 
+// Generic kernel: flattened logical grid, item / chunk fastest, laid out so
+// that the chunks / work items of one row block run on one XCD: a row
+// block's weights are read from HBM once and re-read from that XCD's L2.
 template <int MODE, int TPC>
 __device__ __forceinline__ bool tile_map(const SkinnyArgs &a, int rows_wg, TileMap &m)
 {
@@ -238,13 +240,23 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
     f32x4 *red0 = reinterpret_cast<f32x4 *>(smem + (own_red ? opbytes : 0));
     uint8_t *Ss0 = smem + ((bbytes + 15) & ~15);
 
-    // work item and row-block range (XCD-grouped logical id, item fastest)
-    const int lid = xcd_logical(blockIdx.x, gridDim.x);
+    // Work item and row blocks.  GEMM: XCD-grouped logical id, token chunks
+    // fastest, so the chunks of a row block share its weights in one XCD's
+    // L2.  Expert bank: plain dispatch order, row blocks fastest, and each
+    // workgroup walks row blocks nrbg apart, so the workgroups resident at
+    // any moment read a few experts' matrices front to back in adjacent
+    // blocks (measured, 64-expert decode layer: 110.6 us with items
+    // fastest, 102.7 with row blocks fastest, 102.0 with the strided walk;
+    // XCD-grouped ids over the real items 106.0).  The surplus workgroups of
+    // the upper-bound grid are dispatched last and exit.
+    const int nrbg = (a.nrb + a.rbw - 1) / a.rbw;
+    const int lid = MODE == MODE_GEMM ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
     TileMap tm;
-    if (!item_map<MODE, TPC>(a, lid % a.nch, tm))
+    if (!item_map<MODE, TPC>(a, MODE == MODE_GEMM ? lid % a.nch : lid / nrbg, tm))
         return;
-    const int rb_first = (lid / a.nch) * a.rbw;
-    const int rb_end = min(a.nrb, rb_first + a.rbw);
+    const int rstride = MODE == MODE_GEMM ? 1 : nrbg;
+    const int rb_first = MODE == MODE_GEMM ? (lid / a.nch) * a.rbw : lid % nrbg;
+    const int rb_end = min(a.nrb, rb_first + a.rbw * rstride);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave / nwk, wk = wave % nwk;
@@ -345,10 +357,10 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
     const __bf16 *bb = Bs + b_row<XBF>(li, tm.ntok) * bstride + wk * KW + ls * 32;
     const int srow_off = (mat * rows_wg + tile * 16 + li) * sstride + wk * (KW / 32);
     constexpr int UPW = KW / 512; // 512-column units per wave
-    for (int rb = rb_first; rb < rb_end; ++rb) {
+    for (int rb = rb_first; rb < rb_end; rb += rstride) {
         tm.row0 = rb * rows_wg;
-        const bool more = rb + 1 < rb_end;
-        const int par = (rb - rb_first) & 1;
+        const bool more = rb + rstride < rb_end;
+        const int par = ((rb - rb_first) / rstride) & 1;
         const uint8_t *srow = Ss0 + par * ssbytes + srow_off;
         f32x4 *red = red0 + par * (redbytes / 16);
         // next row block: scales, then weights (younger than everything this
@@ -363,16 +375,16 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
         constexpr bool LATE = MODE != MODE_GEMM;
         u32x4 cwn[LATE ? 1 : LS];
         auto load_next_codes = [&](u32x4 *dst) {
-            const uint8_t *arow = arow_of(tm.row0 + rows_wg);
+            const uint8_t *arow = arow_of(tm.row0 + rstride * rows_wg);
 #pragma unroll
             for (int L = 0; L < LS; ++L)
                 dst[L] = *reinterpret_cast<const u32x4 *>(arow + L * 64);
         };
         if (more) {
             if constexpr (DS)
-                load_sd(tm.row0 + rows_wg, sdn);
+                load_sd(tm.row0 + rstride * rows_wg, sdn);
             else
-                sv = load_scales(tm.row0 + rows_wg);
+                sv = load_scales(tm.row0 + rstride * rows_wg);
             if constexpr (!LATE)
                 load_next_codes(cwn);
         }

@@ -139,13 +139,13 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     const int nsteps = C / TKS; // a multiple of 4 (cols % 512 == 0)
     const int nunits = nsteps / 4;
 
-    // ---- work item (XCD-grouped logical id).  GEMM: token chunks fastest,
-    // so the chunks of a row block share its weights in one XCD's L2.
-    // Expert bank: row blocks fastest over the n_work real items only (the
-    // grid is sized by an upper bound; the surplus workgroups, dispatched
-    // last, exit), so an item's gathered activation rows stay in one XCD's
-    // L2 across its row blocks and the items of a hot expert run side by
-    // side on one XCD.
+    // ---- work item.  GEMM: XCD-grouped logical id, token chunks fastest, so
+    // the chunks of a row block share its weights in one XCD's L2.  Expert
+    // bank: plain dispatch order, row blocks fastest over the n_work real
+    // items (the grid is sized by an upper bound; the surplus workgroups,
+    // dispatched last, exit), so the resident workgroups stream adjacent
+    // blocks of a few experts' matrices (measured, 256-expert prefill layer:
+    // 1563 us with XCD-grouped ids, 1528 us in dispatch order).
     int sub, row0;
     if (MODE == MODE_GEMM) {
         const int lid = xcd_logical(blockIdx.x, gridDim.x);
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
         const int real = *a.n_work * nrb;
         if ((int)blockIdx.x >= real)
             return;
-        const int lid = xcd_logical(blockIdx.x, real);
+        const int lid = blockIdx.x;
         sub = lid / nrb;
         row0 = (lid % nrb) * RB;
     }
