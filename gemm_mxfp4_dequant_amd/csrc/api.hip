@@ -91,6 +91,7 @@ constexpr int TILED_NW_MOE = 8;
 constexpr int TILED_RT_GATEUP = 1; // four 32 KB LDS stages
 constexpr int TILED_RT_DOWN = 2;   // one activation slab serves 256 rows
 constexpr int TILED_NW_GEMM = 4;
+constexpr int TILED_NW_GEMM_TALL = 8; // 128-row blocks when the grid stays full
 constexpr int TILED_NC = 4;
 constexpr int TILED_MIN_TOKENS = 8;
 constexpr int TILED_MIN_WGS = 192; // GEMM: tiled only with ~one workgroup per CU
@@ -461,6 +462,15 @@ int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_d
         const int64_t nch = tnch;
         if (twgs > ((int64_t)1 << 31) - 1)
             return fail(MXFP4_EINVAL, "rows * b too large for one launch");
+        // Twice the rows per workgroup (one activation slab serves 128 rows)
+        // while the grid keeps TILED_MIN_WGS workgroups (measured, 14336 x
+        // 4096 fp32 b = 32, two 16-token chunks: 448 workgroups of 64 rows
+        // 24.5 us, 224 of 128 rows 20.4 us; at b = 16 and bf16 b = 64 the 112
+        // workgroups of 128 rows lose, 20.5 / 26.8 us against 17.6 / 19.3).
+        const int nw = tnch * ((rows + mx::tiled_rows_per_wg(TILED_NW_GEMM_TALL, 1) - 1) /
+                               mx::tiled_rows_per_wg(TILED_NW_GEMM_TALL, 1)) >= TILED_MIN_WGS
+                           ? TILED_NW_GEMM_TALL
+                           : TILED_NW_GEMM;
         mx::SkinnyArgs a = {};
         a.w0 = static_cast<const uint8_t *>(w);
         a.rows = (int)rows;
@@ -471,7 +481,7 @@ int mxfp4_gemm(const void *w, int64_t rows, int64_t cols, const void *x, int x_d
         a.y = y;
         a.y_bf16 = y_dtype == MXFP4_BF16;
         return launched(
-            mx::tiled_launch(mx::MODE_GEMM, xbf, TILED_NW_GEMM, 1, nc, a, (hipStream_t)stream),
+            mx::tiled_launch(mx::MODE_GEMM, xbf, nw, 1, nc, a, (hipStream_t)stream),
             "gemm");
     }
     const int tpc = mx::skinny_pick_tpc(mx::MODE_GEMM, xbf, (int)cols, b < maxc ? (int)b : maxc);

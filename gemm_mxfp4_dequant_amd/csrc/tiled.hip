@@ -420,10 +420,12 @@ struct TEntry {
     MX_TX(MODE, NW, RT, NC), MX_T(MODE, 0, NW, RT, NC, 1), MX_T(MODE, 1, NW, RT, NC, 1)
 // expert bank: gate/up 8 waves x 1 row tile (four 32 KB stages), down 8 x 2
 // (one activation slab serves 256 rows: 1.67 -> 1.59 ms on the prefill bank);
-// GEMM: 4 waves x 1 row tile (more workgroups on 14336-row weights)
+// GEMM: 4 waves x 1 row tile (more workgroups on 14336-row weights), or 8
+// when the grid keeps enough workgroups
 const TEntry kTiled[] = {
     MX_TXB(MODE_GATEUP, 8, 1, 4), MX_TXB(MODE_DOWN, 8, 2, 4),
     MX_TX(MODE_GEMM, 4, 1, 4), MX_TX(MODE_GEMM, 4, 1, 2),
+    MX_TX(MODE_GEMM, 8, 1, 4), MX_TX(MODE_GEMM, 8, 1, 2),
 };
 
 const TEntry *tfind(int mode, bool xbf, int nw, int rt, int nc, bool pt)
