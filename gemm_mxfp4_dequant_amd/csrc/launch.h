@@ -51,6 +51,7 @@ static_assert(sizeof(SkinnyArgs) == 128, "SkinnyArgs layout: see reserved_");
 struct SkinnyShape {
     int kw, tpc, nr, threads, rows_per_wg, rbw;
     size_t lds;
+    int64_t persist_wgs; // expert bank: the grid the items share (0: GEMM)
 };
 
 // Tokens per workgroup for a call that wants `want` columns (fits LDS).

@@ -242,21 +242,34 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
 
     // Work item and row blocks.  GEMM: XCD-grouped logical id, token chunks
     // fastest, so the chunks of a row block share its weights in one XCD's
-    // L2.  Expert bank: plain dispatch order, row blocks fastest, and each
-    // workgroup walks row blocks nrbg apart, so the workgroups resident at
-    // any moment read a few experts' matrices front to back in adjacent
-    // blocks (measured, 64-expert decode layer: 110.6 us with items
-    // fastest, 102.7 with row blocks fastest, 102.0 with the strided walk;
-    // XCD-grouped ids over the real items 106.0).  The surplus workgroups of
-    // the upper-bound grid are dispatched last and exit.
-    const int nrbg = (a.nrb + a.rbw - 1) / a.rbw;
+    // L2; a.rbw consecutive row blocks per workgroup.  Expert bank: plain
+    // dispatch order, row blocks fastest, each workgroup walking its item's
+    // row blocks nrbg apart, so the workgroups resident at any moment read a
+    // few experts' matrices front to back in adjacent blocks (measured,
+    // 64-expert decode layer: 110.6 us with items fastest, 102.7 with row
+    // blocks fastest, 102.0 with the strided walk; XCD-grouped ids over the
+    // real items 106.0).  Down: an upper-bound grid of nrbg = nrb / a.rbw
+    // workgroups per item; the surplus is dispatched last and exits.
+    // Gate/up: a grid of about one round of resident workgroups (at least
+    // one per item bound) that the n_work real items share on the device,
+    // nrbg = grid / n_work each, so that no last round of a few long
+    // workgroups is left (measured: gate/up 64.8 -> 63.1 us; the shorter
+    // down workgroups were slower so, 29.4 -> 32.8 us).
     const int lid = MODE == MODE_GEMM ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    const int nrbg = MODE == MODE_GEMM   ? 1
+                     : MODE == MODE_DOWN ? (a.nrb + a.rbw - 1) / a.rbw
+                                         : min(a.nrb, max(1, (int)gridDim.x / max(1, *a.n_work)));
     TileMap tm;
     if (!item_map<MODE, TPC>(a, MODE == MODE_GEMM ? lid % a.nch : lid / nrbg, tm))
         return;
     const int rstride = MODE == MODE_GEMM ? 1 : nrbg;
     const int rb_first = MODE == MODE_GEMM ? (lid / a.nch) * a.rbw : lid % nrbg;
-    const int rb_end = min(a.nrb, rb_first + a.rbw * rstride);
+    // (a gate/up workgroup without reduction buffers of its own runs in a
+    // grid with a workgroup per row block and takes one block)
+    const int rb_end = MODE == MODE_GEMM   ? min(a.nrb, rb_first + a.rbw)
+                       : MODE == MODE_DOWN ? min(a.nrb, rb_first + a.rbw * rstride)
+                       : a.rbw == 1        ? min(a.nrb, rb_first + 1)
+                                           : a.nrb;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave / nwk, wk = wave % nwk;
@@ -694,6 +707,23 @@ int skinny_pick_tpc(int mode, bool xbf, int cols, int want)
 
 namespace {
 
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0)
+        return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+        n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 // Workgroups of this kernel that fit on one CU (registers, LDS, waves), as
 // the runtime computes it; cached per (kernel, threads, LDS).
 int wgs_per_cu(const Entry *e, int threads, size_t lds)
@@ -783,7 +813,23 @@ SkinnyShape skinny_shape(int mode, bool xbf, int rows, int cols, int tpc, int64_
         s.lds = lds_generic(mode, xbf, cols, tpc);
     }
     s.rows_per_wg = s.nr * 16;
-    if (s.kw) {
+    s.persist_wgs = 0;
+    if (s.kw && mode == MODE_GATEUP) {
+        // Expert bank: a grid of about one round of resident workgroups,
+        // shared by the items on the device (reduction and scale buffers of
+        // their own, so that a workgroup walks row blocks with one barrier
+        // each).
+        const Entry *e = find(mode, xbf, s.kw, tpc, s.threads <= 512 ? 8 : 16);
+        const size_t lds2 = lds_splitk(mode, xbf, cols, s.kw, tpc, s.nr, 2);
+        const int64_t nrb = (rows + s.rows_per_wg - 1) / s.rows_per_wg;
+        if (e && nrb > 1 && lds2 <= (size_t)LDS_MAX) {
+            s.rbw = 2;
+            s.lds = lds2;
+        }
+        const int per_cu = e ? wgs_per_cu(e, s.threads, s.lds) : 1;
+        s.persist_wgs = s.rbw > 1 ? std::max<int64_t>((int64_t)device_cus() * per_cu, items)
+                                  : nrb * items;
+    } else if (s.kw) {
         // Walk several row blocks per workgroup while the grid stays above
         // RB_MIN_WGS workgroups and the workgroups per CU do not drop (the
         // walking kernel needs its own reduction region): the tokens are
@@ -808,6 +854,8 @@ SkinnyShape skinny_shape(int mode, bool xbf, int rows, int cols, int tpc, int64_
 int64_t skinny_blocks(const SkinnyShape &s, int rows, int nch)
 {
     const int64_t nrb = (rows + s.rows_per_wg - 1) / s.rows_per_wg;
+    if (s.persist_wgs > 0) // expert bank: the items share the grid on the device
+        return std::min(s.persist_wgs, nrb * nch);
     return (nrb + s.rbw - 1) / s.rbw * nch;
 }
 
