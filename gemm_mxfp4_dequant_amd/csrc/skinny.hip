@@ -160,6 +160,35 @@ __device__ __forceinline__ void store_unit(__bf16 *Bs, int bstride, int ntok, in
     }
 }
 
+// Row 4 ls + c of the final tile -> outputs: g = D[4 ls + c][li] of the
+// (gate) tile, u the up tile (GATEUP only); the same arithmetic as
+// store_tile for one accumulator component.
+template <int MODE, bool XBF>
+__device__ __forceinline__ void store_row(const SkinnyArgs &a, const TileMap &tm, float g, float u,
+                                          int tile, int lane, int c)
+{
+    const int li = lane & 15, ls = lane >> 4;
+    if (!XBF) {
+        g += dpp_row_ror8(g);
+        if (MODE == MODE_GATEUP)
+            u += dpp_row_ror8(u);
+    }
+    const bool col_ok = XBF ? (li < tm.ntok) : (li < 8 && li < tm.ntok);
+    const int r = tm.row0 + tile * 16 + 4 * ls + c;
+    if (!col_ok || r >= a.rows)
+        return;
+    const int64_t orow = tm.slot0 + li; // token (GEMM) or slot (MoE)
+    float v = g;
+    if (MODE == MODE_GATEUP) {
+        const float pw = a.v41 ? a.pair_w[a.pair_of_slot[orow]] : 0.0f;
+        v = a.v41 ? swiglu_v41(g, u, pw, a.lim) : silu(g) * u;
+    }
+    if (MODE != MODE_DOWN && a.y_bf16)
+        reinterpret_cast<uint16_t *>(a.y)[orow * a.rows + r] = f32_to_bf16_bits(v);
+    else
+        reinterpret_cast<float *>(a.y)[orow * a.rows + r] = v;
+}
+
 // Final tile -> outputs.  g[i] = D[4*ls + i][li] of the (gate) tile, u the
 // up tile (GATEUP only).  For fp32 inputs the lo column li+8 is folded into
 // column li first.
@@ -440,18 +469,29 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
         if (!DS && more && tid < sunits)
             *reinterpret_cast<u32x4 *>(Ss0 + (par ^ 1) * ssbytes + srr * sstride + sc16 * 16) = sv;
         __syncthreads();
-        if (wk == 0 && mat == 0) {
-            f32x4 g = red[(wr * nun) * 64 + lane];
-            for (int k = 1; k < nun; ++k)
-                g += red[(wr * nun + k) * 64 + lane];
-            f32x4 u = g;
-            if (MODE == MODE_GATEUP) {
-                const int wu = NR + tile;
-                u = red[(wu * nun) * 64 + lane];
-                for (int k = 1; k < nun; ++k)
-                    u += red[(wu * nun + k) * 64 + lane];
+        // The tile's epilogue (unit sums, hi + lo fold, activation, store)
+        // is split over up to four of its waves by accumulator component c
+        // (output rows 4 ls + c), so that no single wave trails the others
+        // into the next block's barrier.
+        {
+            const int q = mat * nwk + wk; // this wave's rank among the tile's waves
+            const int nred = min(4, NMAT * nwk);
+            if (q < nred) {
+                const float *rf = reinterpret_cast<const float *>(red);
+                for (int c = q; c < 4; c += nred) {
+                    float g = rf[((tile * nun) * 64 + lane) * 4 + c];
+                    for (int k = 1; k < nun; ++k)
+                        g += rf[((tile * nun + k) * 64 + lane) * 4 + c];
+                    float u = g;
+                    if (MODE == MODE_GATEUP) {
+                        const int wu = NR + tile;
+                        u = rf[((wu * nun) * 64 + lane) * 4 + c];
+                        for (int k = 1; k < nun; ++k)
+                            u += rf[((wu * nun + k) * 64 + lane) * 4 + c];
+                    }
+                    store_row<MODE, XBF>(a, tm, g, u, tile, lane, c);
+                }
             }
-            store_tile<MODE, XBF>(a, tm, g, u, tile, lane);
         }
         if (!more)
             break;
