@@ -285,7 +285,17 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
     g.token_of_slot = tos;
     g.work = work;
     g.n_work = n_work;
-    TRY(launched(mx::group_launch(g, st), "group"));
+    // Decode-sized routing (at most 64 pairs) into the split-K gate/up
+    // kernel: it groups the routing itself (every workgroup ranks the pairs
+    // with one wave; workgroup 0 writes the tables the down and combine
+    // kernels read), in place of the grouping kernel (measured, 64-expert
+    // decode layer: 96.9 -> 94.4 us).
+    const mx::SkinnyShape sh_gu =
+        tiled ? mx::SkinnyShape{}
+              : mx::skinny_shape(mx::MODE_GATEUP, xbf, (int)inter, (int)hidden, tpc, max_work);
+    const bool fuse = !tiled && !h_in && !h_out && P <= 64 && sh_gu.kw != 0;
+    if (!fuse)
+        TRY(launched(mx::group_launch(g, st), "group"));
 
     const int64_t tbytes = mxfp4_nbytes(inter, hidden);
     if (!h_in) {
@@ -312,9 +322,12 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
                                           TILED_NC, a, st),
                          "gate/up"));
         } else {
-            const mx::SkinnyShape sh =
-                mx::skinny_shape(mx::MODE_GATEUP, xbf, (int)inter, (int)hidden, tpc, max_work);
-            TRY(launched(mx::skinny_launch(mx::MODE_GATEUP, xbf, sh, a, st), "gate/up"));
+            if (fuse) {
+                a.fuse_group = 1 | (P << 1) | ((int)top_k << 8) | ((int)n_experts << 14);
+                a.token_of_slot = topk_ids;
+                a.pair_of_slot = slot; // slot_of_pair, written by the kernel
+            }
+            TRY(launched(mx::skinny_launch(mx::MODE_GATEUP, xbf, sh_gu, a, st), "gate/up"));
         }
         if (h_out)
             TRY(launched(mx::copy_launch(h_out, h, (size_t)P * inter * (xbf ? 2 : 4), st),

@@ -36,14 +36,19 @@ struct SkinnyArgs {
     // of n_experts pointers; an entry may point to device memory or to
     // device-mapped pinned host memory) instead of contiguous banks.
     int ptr_table;
-    // Pads the struct to 128 bytes, so the hidden launch arguments the
-    // compiler appends (grid and workgroup sizes) start at offset 128.
-    // Measured against the unpadded 120 bytes, same code otherwise: 4096 x
-    // 4096 matvec 5.04 -> 4.85 us, b = 8 6.97 -> 6.77 us, 64-expert decode
-    // -0.4 %, 14336 x 4096 b = 8 +0.9 %.
-    int reserved_;
+    // GATEUP (split-K kernel): 0, or routing that the kernel groups itself
+    // (at most 64 pairs), packed as 1 | P << 1 | top_k << 8 | n_experts << 14.
+    // Then token_of_slot holds the routing ids [P] and pair_of_slot the
+    // slot_of_pair table [P], which workgroup 0 writes together with work and
+    // n_work for the down and combine kernels.
+    // This last field also pads the struct to 128 bytes, so the hidden
+    // launch arguments the compiler appends (grid and workgroup sizes) start
+    // at offset 128.  Measured against the unpadded 120 bytes, same code
+    // otherwise: 4096 x 4096 matvec 5.04 -> 4.85 us, b = 8 6.97 -> 6.77 us,
+    // 64-expert decode -0.4 %, 14336 x 4096 b = 8 +0.9 %.
+    int fuse_group;
 };
-static_assert(sizeof(SkinnyArgs) == 128, "SkinnyArgs layout: see reserved_");
+static_assert(sizeof(SkinnyArgs) == 128, "SkinnyArgs layout: see fuse_group");
 
 // Launch shape of one skinny call: K slab width (0 = generic kernel),
 // tokens per workgroup, row tiles per matrix, threads, row blocks walked by

@@ -57,6 +57,10 @@ struct TileMap {
     int slot0;  // first token (GEMM) / first slot (MoE)
     int row0;   // first output row
     int expert; // MoE expert (0 for GEMM)
+    // GATEUP: token row and routing pair of each token column (global
+    // tables, or this workgroup's own when the kernel groups the routing)
+    const int *rowmap;
+    const int *pairmap;
 };
 
 // Work item `sub` of this workgroup; false if it has none (MoE grids are
@@ -78,7 +82,105 @@ __device__ __forceinline__ bool item_map(const SkinnyArgs &a, int sub, TileMap &
     m.expert = wk.x;
     m.slot0 = wk.y;
     m.ntok = wk.z;
+    m.rowmap = a.token_of_slot + wk.y;
+    m.pairmap = a.pair_of_slot + wk.y;
     return true;
+}
+
+constexpr int FG_KEYBITS = 11;     // keys: expert ids 0..1024, and a dropped pair
+constexpr int FG_DROPPED = 2047;   // key of a dropped pair (above every expert id)
+// LDS of the in-kernel grouping: n_work, expert, slot0, ntok, then the
+// token rows and pairs of up to 16 token columns, then a 64-entry scan
+constexpr int FG_WORDS = 4 + 32 + 64;
+
+// Routing grouped inside the gate/up kernel (one wave, at most 64 pairs):
+// the counting sort of the grouping kernels ("rlx-cpu 0.2.17,
+// src/gguf_matmul.rs", grouped_moe_sort_plan) by wave ballots: experts
+// ascending, pairs in order within an expert, so slots, work items and
+// tables equal the grouping kernel's.  Writes this workgroup's item (of the
+// workgroup grid the items share, as in the split-K kernel) to fz; writer:
+// also the tables the down and combine kernels read.
+__device__ void fused_group(const SkinnyArgs &a, int tpc, int lid, int grid, bool writer, int *fz)
+{
+    const int lane = threadIdx.x & 63;
+    const int P = (a.fuse_group >> 1) & 127;
+    const int K = (a.fuse_group >> 8) & 63;
+    const int E = (a.fuse_group >> 14) & 2047;
+    int e = -1;
+    if (lane < P) {
+        e = a.token_of_slot[lane]; // the routing ids
+        if (e < 0 || e >= E)
+            e = -1;
+    }
+    const bool valid = e >= 0;
+    const int key = valid ? e : FG_DROPPED;
+    // lanes with a smaller key (lt) and with the same key (eq), among valid
+    uint64_t lt = 0, eq = __ballot(valid);
+#pragma unroll
+    for (int b = FG_KEYBITS - 1; b >= 0; --b) {
+        const int bit = (key >> b) & 1;
+        const uint64_t ones = __ballot(bit);
+        if (bit) {
+            lt |= eq & ~ones;
+            eq &= ones;
+        } else {
+            eq &= ~ones;
+        }
+    }
+    const int rank = __popcll(eq & ((1ull << lane) - 1));
+    const int start = __popcll(lt); // first slot of this expert
+    const int slot = valid ? start + rank : -1;
+    const int cnt = __popcll(eq);
+    const bool leader = valid && rank == 0;
+    const int nit = leader ? (cnt + tpc - 1) / tpc : 0;
+    // items before each expert: exclusive scan of the items in slot order
+    int *scan = fz + 36;
+    scan[lane] = 0;
+    if (leader)
+        scan[start] = nit;
+    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's LDS stores
+    const int v = scan[lane];
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d)
+            incl += o;
+    }
+    const int n_work = __shfl(incl, 63, 64);
+    const int ibase = __shfl(incl - v, start & 63, 64); // for leaders
+    // this workgroup's item
+    const int nrbg = min(a.nrb, max(1, grid / max(1, n_work)));
+    const int sub = lid / nrbg;
+    const uint64_t mine = __ballot(leader && sub >= ibase && sub < ibase + nit);
+    int ex = -1, slot0 = 0, ntok = 0;
+    if (mine) {
+        const int L = __ffsll((long long)mine) - 1;
+        const int c = sub - __shfl(ibase, L, 64);
+        ex = __shfl(e, L, 64);
+        slot0 = __shfl(start, L, 64) + c * tpc;
+        ntok = min(tpc, __shfl(cnt, L, 64) - c * tpc);
+    }
+    if (valid && slot >= slot0 && slot < slot0 + ntok) {
+        fz[4 + slot - slot0] = lane / K;       // token row
+        fz[4 + 16 + slot - slot0] = lane;      // routing pair
+    }
+    if (lane == 0) {
+        fz[0] = n_work;
+        fz[1] = ex;
+        fz[2] = slot0;
+        fz[3] = ntok;
+    }
+    if (writer) {
+        if (lane < P)
+            const_cast<int *>(a.pair_of_slot)[lane] = slot; // slot_of_pair
+        if (leader)
+            for (int c = 0; c < nit; ++c)
+                reinterpret_cast<int4 *>(const_cast<int *>(a.work))[ibase + c] =
+                    int4{e, start + c * tpc, min(tpc, cnt - c * tpc), 0};
+        if (lane == 0)
+            *const_cast<int *>(a.n_work) = n_work;
+    }
 }
 
 // Generic kernel: flattened logical grid, item / chunk fastest, laid out so
@@ -96,11 +198,11 @@ __device__ __forceinline__ bool tile_map(const SkinnyArgs &a, int rows_wg, TileM
 
 // Activation row of token column t.
 template <int MODE>
-__device__ __forceinline__ int64_t token_row(const SkinnyArgs &a, int slot0, int t)
+__device__ __forceinline__ int64_t token_row(const TileMap &tm, int t)
 {
     if (MODE == MODE_GATEUP)
-        return a.token_of_slot[slot0 + t];
-    return slot0 + t;
+        return tm.rowmap[t];
+    return tm.slot0 + t;
 }
 
 // LDS operand row read by lane column j: hi rows 0..ntok-1 and lo rows
@@ -119,10 +221,10 @@ __device__ __forceinline__ int b_row(int j, int ntok)
 
 // Load the 8 activation elements of unit (t, seg) into v (bf16: 4 words).
 template <int MODE, bool XBF>
-__device__ __forceinline__ void load_unit(const SkinnyArgs &a, int slot0, int t, int seg, int C,
-                                          float *v)
+__device__ __forceinline__ void load_unit(const SkinnyArgs &a, const TileMap &tm, int t, int seg,
+                                          int C, float *v)
 {
-    const int64_t row = token_row<MODE>(a, slot0, t);
+    const int64_t row = token_row<MODE>(tm, t);
     if (XBF) {
         const u32x4 w = *reinterpret_cast<const u32x4 *>(
             reinterpret_cast<const uint16_t *>(a.x) + row * C + seg * 8);
@@ -180,7 +282,7 @@ __device__ __forceinline__ void store_row(const SkinnyArgs &a, const TileMap &tm
     const int64_t orow = tm.slot0 + li; // token (GEMM) or slot (MoE)
     float v = g;
     if (MODE == MODE_GATEUP) {
-        const float pw = a.v41 ? a.pair_w[a.pair_of_slot[orow]] : 0.0f;
+        const float pw = a.v41 ? a.pair_w[tm.pairmap[li]] : 0.0f;
         v = a.v41 ? swiglu_v41(g, u, pw, a.lim) : silu(g) * u;
     }
     if (MODE != MODE_DOWN && a.y_bf16)
@@ -211,7 +313,7 @@ __device__ __forceinline__ void store_tile(const SkinnyArgs &a, const TileMap &t
     const int R = a.rows;
     const int rbase = tm.row0 + tile * 16 + 4 * ls;
     const int64_t orow = tm.slot0 + li; // token (GEMM) or slot (MoE)
-    const float pw = (MODE == MODE_GATEUP && a.v41) ? a.pair_w[a.pair_of_slot[orow]] : 0.0f;
+    const float pw = (MODE == MODE_GATEUP && a.v41) ? a.pair_w[tm.pairmap[li]] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = rbase + i;
@@ -284,13 +386,33 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
     // nrbg = grid / n_work each, so that no last round of a few long
     // workgroups is left (measured: gate/up 64.8 -> 63.1 us; the shorter
     // down workgroups were slower so, 29.4 -> 32.8 us).
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lid = MODE == MODE_GEMM ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
-    const int nrbg = MODE == MODE_GEMM   ? 1
-                     : MODE == MODE_DOWN ? (a.nrb + a.rbw - 1) / a.rbw
-                                         : min(a.nrb, max(1, (int)gridDim.x / max(1, *a.n_work)));
     TileMap tm;
-    if (!item_map<MODE, TPC>(a, MODE == MODE_GEMM ? lid % a.nch : lid / nrbg, tm))
-        return;
+    int nrbg;
+    __shared__ int fz[FG_WORDS];
+    if (MODE == MODE_GATEUP && a.fuse_group) {
+        // the routing grouped here (no grouping kernel before this one):
+        // one wave ranks the pairs, the workgroup reads its item from LDS
+        if (wave == 0)
+            fused_group(a, TPC, lid, (int)gridDim.x, blockIdx.x == 0, fz);
+        __syncthreads();
+        if (fz[3] <= 0)
+            return;
+        nrbg = min(a.nrb, max(1, (int)gridDim.x / max(1, fz[0])));
+        tm.row0 = 0;
+        tm.expert = fz[1];
+        tm.slot0 = fz[2];
+        tm.ntok = fz[3];
+        tm.rowmap = fz + 4;
+        tm.pairmap = fz + 4 + 16;
+    } else {
+        nrbg = MODE == MODE_GEMM   ? 1
+               : MODE == MODE_DOWN ? (a.nrb + a.rbw - 1) / a.rbw
+                                   : min(a.nrb, max(1, (int)gridDim.x / max(1, *a.n_work)));
+        if (!item_map<MODE, TPC>(a, MODE == MODE_GEMM ? lid % a.nch : lid / nrbg, tm))
+            return;
+    }
     const int rstride = MODE == MODE_GEMM ? 1 : nrbg;
     const int rb_first = MODE == MODE_GEMM ? (lid / a.nch) * a.rbw : lid % nrbg;
     // (a gate/up workgroup without reduction buffers of its own runs in a
@@ -300,7 +422,6 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
                        : a.rbw == 1        ? min(a.nrb, rb_first + 1)
                                            : a.nrb;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave / nwk, wk = wave % nwk;
     const int mat = wr / NR, tile = wr % NR;
     const int li = lane & 15, ls = lane >> 4;
@@ -325,7 +446,7 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
             const int u = tid + q * NT;
             if (u < units) {
                 const int t = u / segs;
-                load_unit<MODE, XBF>(a, tm.slot0, t, u - t * segs, C, xv[q]);
+                load_unit<MODE, XBF>(a, tm, t, u - t * segs, C, xv[q]);
             }
         }
     };
@@ -389,7 +510,7 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
     for (int u = tid + UMAX * NT; u < units; u += NT) { // beyond the up-front batch
         float v[8];
         const int t = u / segs;
-        load_unit<MODE, XBF>(a, tm.slot0, t, u - t * segs, C, v);
+        load_unit<MODE, XBF>(a, tm, t, u - t * segs, C, v);
         store_unit<XBF>(Bs, bstride, tm.ntok, t, u - t * segs, v);
     }
     if (!DS && tid < sunits)
@@ -549,7 +670,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_generic(SkinnyArgs a)
     // activations -> LDS (zero beyond C up to cpad)
     const int segs = cpad / 8;
     for (int t = 0; t < tm.ntok; ++t) {
-        const int64_t row = token_row<MODE>(a, tm.slot0, t);
+        const int64_t row = token_row<MODE>(tm, t);
         for (int seg = tid; seg < segs; seg += NT) {
             float v[8];
             const int c = seg * 8;
@@ -638,7 +759,11 @@ __global__ __launch_bounds__(NW * 64) void skinny_generic(SkinnyArgs a)
 namespace {
 
 constexpr int NW_GENERIC = 4;
-constexpr int LDS_MAX = 160 * 1024;
+// Dynamic LDS per workgroup: the CU's 160 KB less 512 bytes for the static
+// LDS of the gate/up kernels that group the routing themselves (400 bytes),
+// so that one opt-in value fits every kernel of the table.
+constexpr int LDS_MAX = 160 * 1024 - 512;
+static_assert(FG_WORDS * 4 <= 512, "static LDS of the in-kernel grouping");
 // Row blocks per split-K workgroup: at most RB_MAX, and only while the grid
 // keeps RB_MIN_WGS workgroups (4 per CU; 8 before the reduction was
 // double-buffered: 64-expert decode layer 112.2 -> 111.3 us with 4).
@@ -782,13 +907,17 @@ int wgs_per_cu(const Entry *e, int threads, size_t lds)
         if (cache[i].e == e && cache[i].threads == threads && cache[i].lds == lds)
             return cache[i].n;
     int n = 0;
-    if (lds > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(e->fn),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, LDS_MAX);
+    // (a failed query leaves no error behind for the next launch check)
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(e->fn),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_MAX) != hipSuccess)
+        (void)hipGetLastError();
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(e->fn),
                                                      threads, lds) != hipSuccess ||
-        n < 1)
+        n < 1) {
+        (void)hipGetLastError();
         n = 1;
+    }
     if (used < 128)
         cache[used++] = Key{e, threads, lds, n};
     return n;

@@ -266,3 +266,59 @@ def test_token_alone_equals_batch_bitwise(m, xd, E, H, I, T, K):
         o1 = host(m.moe_experts_mxfp4(d["gate"], d["up"], d["down"], E, H, I, d["x"][t:t + 1],
                                       d["ids"][t:t + 1], d["w"][t:t + 1]))
         assert np.array_equal(o1[0], ob[t]), t
+
+
+@pytest.mark.parametrize("T,K,E,xdt,drop", [(8, 6, 64, "f32", False), (8, 8, 64, "f32", True),
+                                            (1, 4, 16, "bf16", False), (16, 4, 40, "f32", True),
+                                            (13, 5, 1024, "f32", False)])
+def test_fused_grouping_equals_grouping_kernel(m, T, K, E, xdt, drop):
+    """Routing of at most 64 pairs is grouped inside the gate/up kernel (each
+    workgroup ranks the pairs itself; workgroup 0 writes the tables for down
+    and combine); the staged entry point, asked for h, runs the grouping
+    kernel instead.  Both must give the same output bit for bit, including
+    dropped pairs, a single token, ragged pair counts (13 x 5 = 65 pairs
+    takes the grouping kernel on both sides) and a 1024-expert bank."""
+    H, I = 512, 64
+    c = inputs.moe_case(900 + T * K + E, E, H, I, T, K, xdt, "softmax", scale_lo=110,
+                        scale_hi=124)
+    ids = c["ids"].copy().reshape(-1)
+    if drop:
+        ids[::5] = -1
+        ids[3::7] = E + 2
+    c["ids"] = ids.reshape(T, K).astype(np.int32)
+    d = upload(c)
+    fused = m.moe_experts_mxfp4(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"], d["w"])
+    h = torch.empty((T * K, I), dtype=torch.bfloat16 if xdt == "bf16" else torch.float32,
+                    device="cuda")
+    staged, _ = m.moe_experts_mxfp4_stages(d["gate"], d["up"], d["down"], E, H, I, d["x"],
+                                           d["ids"], d["w"], out=torch.empty_like(fused), h_out=h)
+    torch.cuda.synchronize()
+    a, b = host(fused), host(staged)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    # and a rerun of the fused path (its tables rewritten in the same workspace)
+    again = host(m.moe_experts_mxfp4(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"],
+                                     d["w"]))
+    assert np.array_equal(a.view(np.uint16), again.view(np.uint16))
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_fused_grouping_v41(m, shared):
+    """The V4.1 bank on decode-sized routing: the fused grouping's route
+    weights (read through its own pair table) and the shared expert's
+    augmented routing give the staged (grouping-kernel) result bit for bit."""
+    E, H, I, T, K = 32, 1024, 512, 6, 7
+    c = inputs.moe_case(77 + int(shared), E + int(shared), H, I, T, K, "bf16", "softmax",
+                        scale_lo=110, scale_hi=125)
+    ids = c["ids"].copy()
+    ids[ids >= E] = ids[ids >= E] % E
+    c["ids"] = ids.astype(np.int32)
+    d = upload(c)
+    fused = m.moe_experts_mxfp4_v41(d["gate"], d["up"], d["down"], E, H, I, d["x"], d["ids"],
+                                    d["w"], swiglu_limit=7.0, has_shared=shared)
+    h = torch.empty((T * (K + int(shared)), I), dtype=torch.bfloat16, device="cuda")
+    staged, _ = m.moe_experts_mxfp4_v41_stages(d["gate"], d["up"], d["down"], E, H, I, d["x"],
+                                               d["ids"], d["w"], swiglu_limit=7.0,
+                                               has_shared=shared, out=torch.empty_like(fused),
+                                               h_out=h)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(fused).view(np.uint16), host(staged).view(np.uint16))
