@@ -267,7 +267,7 @@ __device__ __forceinline__ void store_unit(__bf16 *Bs, int bstride, int ntok, in
 // store_tile for one accumulator component.
 template <int MODE, bool XBF>
 __device__ __forceinline__ void store_row(const SkinnyArgs &a, const TileMap &tm, float g, float u,
-                                          int tile, int lane, int c)
+                                          int tile, int lane, int c, float pw)
 {
     const int li = lane & 15, ls = lane >> 4;
     if (!XBF) {
@@ -281,10 +281,8 @@ __device__ __forceinline__ void store_row(const SkinnyArgs &a, const TileMap &tm
         return;
     const int64_t orow = tm.slot0 + li; // token (GEMM) or slot (MoE)
     float v = g;
-    if (MODE == MODE_GATEUP) {
-        const float pw = a.v41 ? a.pair_w[tm.pairmap[li]] : 0.0f;
+    if (MODE == MODE_GATEUP)
         v = a.v41 ? swiglu_v41(g, u, pw, a.lim) : silu(g) * u;
-    }
     if (MODE != MODE_DOWN && a.y_bf16)
         reinterpret_cast<uint16_t *>(a.y)[orow * a.rows + r] = f32_to_bf16_bits(v);
     else
@@ -426,6 +424,11 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
     const int mat = wr / NR, tile = wr % NR;
     const int li = lane & 15, ls = lane >> 4;
     const int R = a.rows;
+    // V4.1 route weight of this lane's token column, read once here rather
+    // than through two dependent loads in every row block's epilogue
+    float opw = 0.0f;
+    if (MODE == MODE_GATEUP && a.v41 && (XBF ? li : (li & 7)) < tm.ntok)
+        opw = a.pair_w[tm.pairmap[XBF ? li : (li & 7)]];
     const uint8_t *A0 =
         MODE == MODE_GEMM ? a.w0 : expert_base<PT>(a.w0, tm.expert, a.expert_stride);
     const uint8_t *A1 =
@@ -610,7 +613,7 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
                         for (int k = 1; k < nun; ++k)
                             u += rf[((wu * nun + k) * 64 + lane) * 4 + c];
                     }
-                    store_row<MODE, XBF>(a, tm, g, u, tile, lane, c);
+                    store_row<MODE, XBF>(a, tm, g, u, tile, lane, c, opw);
                 }
             }
         }
