@@ -19,7 +19,8 @@ struct SkinnyArgs {
     int b;                    // GEMM: tokens
     int nch;                  // GEMM: token chunks; MoE: work item bound
     int nrb;                  // row blocks of rows_per_wg rows (set by skinny_launch)
-    int rbw;                  // row blocks walked by one workgroup (set by skinny_launch)
+    int rbw;                  // row blocks walked by one workgroup (set by skinny_launch;
+                              // -1: one, with reduction buffers of its own)
     void *y;                  // GEMM: y [b][rows]; GATEUP: h [slots][rows]; DOWN: y [slots][rows]
     int y_bf16;               // output element type (GEMM, GATEUP)
     const int *work;          // MoE: int4 {expert, first slot, tokens, 0} per item
@@ -63,7 +64,7 @@ struct SkinnyShape {
 int skinny_pick_tpc(int mode, bool xbf, int cols, int want);
 // Shape for `items` token chunks / work items per row block.
 SkinnyShape skinny_shape(int mode, bool xbf, int rows, int cols, int tpc, int64_t items);
-// Workgroups of a launch: ceil(ceil(rows / rows_per_wg) / rbw) * nch.
+// Workgroups of a launch: ceil(ceil(rows / rows_per_wg) / |rbw|) * nch.
 int64_t skinny_blocks(const SkinnyShape &s, int rows, int nch);
 hipError_t skinny_launch(int mode, bool xbf, const SkinnyShape &s, SkinnyArgs a,
                          hipStream_t stream);

@@ -363,7 +363,11 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
     // 114.4 -> 111.9 us per layer).
     const int opbytes = (NBC * bstride * 2 + 15) & ~15;
     const int redbytes = nwr * nun * 1024;
-    const bool own_red = a.rbw > 1;
+    // (a.rbw = -1: one row block per workgroup, with reduction buffers of
+    // its own all the same, which saves the barrier that protects the
+    // operands from the overlaid reduction)
+    const int rbw = a.rbw < 0 ? -a.rbw : a.rbw;
+    const bool own_red = a.rbw != 1;
     const int ssbytes = (NMAT * rows_wg * sstride + 15) & ~15;
     const int bbytes = own_red ? opbytes + 2 * redbytes : max(opbytes, redbytes);
     f32x4 *red0 = reinterpret_cast<f32x4 *>(smem + (own_red ? opbytes : 0));
@@ -406,17 +410,17 @@ __global__ __launch_bounds__(MAXW * 64) void skinny_splitk(SkinnyArgs a)
         tm.pairmap = fz + 4 + 16;
     } else {
         nrbg = MODE == MODE_GEMM   ? 1
-               : MODE == MODE_DOWN ? (a.nrb + a.rbw - 1) / a.rbw
+               : MODE == MODE_DOWN ? (a.nrb + rbw - 1) / rbw
                                    : min(a.nrb, max(1, (int)gridDim.x / max(1, *a.n_work)));
         if (!item_map<MODE, TPC>(a, MODE == MODE_GEMM ? lid % a.nch : lid / nrbg, tm))
             return;
     }
     const int rstride = MODE == MODE_GEMM ? 1 : nrbg;
-    const int rb_first = MODE == MODE_GEMM ? (lid / a.nch) * a.rbw : lid % nrbg;
+    const int rb_first = MODE == MODE_GEMM ? (lid / a.nch) * rbw : lid % nrbg;
     // (a gate/up workgroup without reduction buffers of its own runs in a
     // grid with a workgroup per row block and takes one block)
-    const int rb_end = MODE == MODE_GEMM   ? min(a.nrb, rb_first + a.rbw)
-                       : MODE == MODE_DOWN ? min(a.nrb, rb_first + a.rbw * rstride)
+    const int rb_end = MODE == MODE_GEMM   ? min(a.nrb, rb_first + rbw)
+                       : MODE == MODE_DOWN ? min(a.nrb, rb_first + rbw * rstride)
                        : a.rbw == 1        ? min(a.nrb, rb_first + 1)
                                            : a.nrb;
 
@@ -1019,6 +1023,15 @@ SkinnyShape skinny_shape(int mode, bool xbf, int rows, int cols, int tpc, int64_
             s.rbw *= 2;
             s.lds = lds;
         }
+        // one block per workgroup: reduction buffers of its own when they
+        // cost no occupancy (one barrier per block instead of two)
+        if (e && s.rbw == 1) {
+            const size_t lds = lds_splitk(mode, xbf, cols, s.kw, tpc, s.nr, 2);
+            if (lds <= (size_t)LDS_MAX && wgs_per_cu(e, s.threads, lds) >= per_cu) {
+                s.rbw = -1;
+                s.lds = lds;
+            }
+        }
     }
     return s;
 }
@@ -1028,7 +1041,8 @@ int64_t skinny_blocks(const SkinnyShape &s, int rows, int nch)
     const int64_t nrb = (rows + s.rows_per_wg - 1) / s.rows_per_wg;
     if (s.persist_wgs > 0) // expert bank: the items share the grid on the device
         return std::min(s.persist_wgs, nrb * nch);
-    return (nrb + s.rbw - 1) / s.rbw * nch;
+    const int rbw = s.rbw < 0 ? -s.rbw : s.rbw;
+    return (nrb + rbw - 1) / rbw * nch;
 }
 
 hipError_t skinny_launch(int mode, bool xbf, const SkinnyShape &s, SkinnyArgs a,
