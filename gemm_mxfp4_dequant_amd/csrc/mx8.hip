@@ -3,7 +3,7 @@
 // one E8M0 power-of-two scale per 32 elements: the OCP MX family that
 // "cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs" names in its module doc).
 //
-//  * mxfp8_quantize_kernel: one thread per 32-element block of a token row;
+//  * mxfp8_quantize_kernel: eight lanes per 32-element block of a token row;
 //    shared exponent E = floor(log2 max|x|) - 8, stored as the byte E + 127
 //    (clamped to [0, 254]); each element is the E4M3 code nearest to
 //    x / 2^E, ties to even, saturating at 448, computed with integer
@@ -19,7 +19,12 @@
 //    owns two 16-row tiles and NC tiles of 16 tokens; its 8 waves each walk
 //    an eighth of K in 128-column steps (the next step's loads in flight
 //    during the current one) into one fp32 accumulator per tile, and the
-//    eight partials are summed through LDS in K order.
+//    eight partials are summed through LDS in K order.  Used for b <= 16
+//    and for widths that are not a multiple of 512.
+//  * gemm_a8_tiled_kernel (b > 16, cols % 512 == 0): 64-row workgroups
+//    that stream the weights and one LDS copy of the token chunk's
+//    quantized activations through a ring of direct global -> LDS loads,
+//    the same operand lanes as above read from LDS.
 //  * Accuracy (the contract of this entry point, not the 1e-4 rule of the
 //    others): the product is the exact product of the weights with the
 //    quantized activations up to the matrix core's accumulation, which adds
@@ -34,6 +39,10 @@ namespace mx {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int N> struct IntTag8 {
+    static constexpr int value = N;
+};
 
 // E4M3 code nearest to v (|v| < 2^9 or saturating), ties to even.
 __device__ __forceinline__ uint32_t e4m3_rne_bits(float v)
@@ -59,74 +68,67 @@ __device__ __forceinline__ uint32_t e4m3_rne_bits(float v)
     return sign | code;
 }
 
+// Eight consecutive lanes share a 32-element block, four elements each: one
+// 16-byte (fp32) or 8-byte (bf16) load per lane, the block's largest
+// magnitude and its non-finite flag combined over the eight lanes, one
+// 4-byte store of codes per lane and the scale byte from the first.
 template <bool XBF>
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const void *x, int64_t blocks,
-                                                             int gpr, uint8_t *q, uint8_t *s)
+                                                             uint8_t *q, uint8_t *s)
 {
-    const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t blk = gid >> 3;
+    const int sub = (int)(gid & 7);
+    // a whole block's lanes are in or out together (blocks * 8 threads)
     if (blk >= blocks)
         return;
-    float v[32];
+    const int64_t e0 = blk * 32 + sub * 4;
+    float v[4];
     if (XBF) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(
-            reinterpret_cast<const uint16_t *>(x) + blk * 32);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 w = src[i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-                v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-            }
-        }
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(x) + e0);
+        v[0] = __uint_as_float(w[0] << 16);
+        v[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+        v[2] = __uint_as_float(w[1] << 16);
+        v[3] = __uint_as_float(w[1] & 0xFFFF0000u);
     } else {
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(x) +
-                                                           blk * 32);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const f32x4 w = src[i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                v[4 * i + j] = w[j];
-        }
+        const f32x4 w = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(x) + e0);
+        v[0] = w[0];
+        v[1] = w[1];
+        v[2] = w[2];
+        v[3] = w[3];
     }
     float amax = 0.0f;
-    bool bad = false;
+    int bad = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 4; ++i) {
         bad |= !__builtin_isfinite(v[i]);
         amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
     }
-    u32x4 out[2];
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, m, 8));
+        bad |= __shfl_xor(bad, m, 8);
+    }
+    uint32_t word = 0;
+    int k = 0;
     if (bad || amax == 0.0f) {
-        s[blk] = bad ? 255 : 0;
-        out[0] = out[1] = u32x4{0u, 0u, 0u, 0u};
+        k = bad ? 255 : 0;
     } else {
         // floor(log2 amax): the exponent field, or for an fp32 subnormal the
         // position of its leading mantissa bit
         const uint32_t ab = __float_as_uint(amax);
         const int ef = (int)(ab >> 23);
         const int fl = ef ? ef - 127 : (31 - __builtin_clz(ab)) - 149;
-        int k = fl - 8 + 127;
+        k = fl - 8 + 127;
         k = k < 0 ? 0 : (k > 254 ? 254 : k);
-        s[blk] = (uint8_t)k;
         const int e = k - 127; // x / 2^e, exact (a power-of-two scaling)
-        uint32_t packed[8];
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                word |= e4m3_rne_bits(__builtin_ldexpf(v[4 * w + j], -e)) << (8 * j);
-            packed[w] = word;
-        }
-        out[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
-        out[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+        for (int j = 0; j < 4; ++j)
+            word |= e4m3_rne_bits(__builtin_ldexpf(v[j], -e)) << (8 * j);
     }
-    u32x4 *dst = reinterpret_cast<u32x4 *>(q + blk * 32);
-    dst[0] = out[0];
-    dst[1] = out[1];
-    (void)gpr;
+    *reinterpret_cast<uint32_t *>(q + e0) = word;
+    if (sub == 0)
+        s[blk] = (uint8_t)k;
 }
 
 constexpr int A8_NWK = 8; // waves per workgroup, each over 1/8 of K
@@ -255,19 +257,188 @@ __global__ __launch_bounds__(A8_NWK * 64) void gemm_a8_kernel(A8Args a)
     }
 }
 
+// The same product on the tiled schedule (cols % 512 == 0): a workgroup of NW
+// waves owns NW 16-row tiles (one per wave) and NC tiles of 16 tokens, and
+// runs the whole K loop in 128-column steps through a ring of four LDS
+// stages filled by direct global -> LDS loads (three steps in flight).  Per
+// step each wave loads its rows' 16 code bytes per lane and its share of the
+// activation slab (16 NC tokens x 128 E4M3 bytes, stored with 16-byte chunk
+// k of token t at position k ^ (t & 7), so that the sixteen lanes reading
+// one B fragment spread over the banks); with the first step of each
+// 512-column unit it also loads the unit's 16 scale bytes of its rows and of
+// one token tile's tokens, which the waves copy to registers at that step.
+// Every wave issues the same loads, so "stage s has landed" is one constant
+// vmcnt wait, then one barrier per step.  Every wave reads the slab from
+// LDS, so each activation byte fetched serves 16 NW rows.  One fp32
+// accumulator per token tile, steps in ascending order.
+//   Measured at 14336 x 4096, b = 64 (bf16 activations, quantize
+// included): scale bytes once per unit instead of 4-byte loads of 16 rows'
+// (or tokens') scales every step, 23.8 -> 18.9 us.  Not kept: rings of six
+// or eight stages (+4 %, +7 %), and K in two parts over eight waves with the
+// parts' sums added through LDS (19.4 us; b = 256: 51.4 -> 59.5 us).
+constexpr int A8T_NS = 4; // ring stages = steps per 512-column unit
+
+template <int NW, int NC> struct A8TLayout {
+    static_assert((2 * NC) % NW == 0 && NC <= NW, "slab and scale loads spread over the waves");
+    static constexpr int CODES = 0;        // [NW][64 lanes][16 B]
+    static constexpr int SLAB = NW * 1024; // [16 NC tokens][8 chunks][16 B]
+    static constexpr int STAGE = SLAB + NC * 16 * 128;
+    static constexpr int XL = 2 * NC / NW; // slab loads per wave
+    static constexpr int GN = 1 + XL;      // loads per wave per step (+2 with a unit's first)
+};
+
+template <int NW, int NC>
+__global__ __launch_bounds__(NW * 64) void gemm_a8_tiled_kernel(A8Args a)
+{
+    using L = A8TLayout<NW, NC>;
+    // one variable per stage: the loads into one stage and the reads of
+    // another are known not to alias
+    __shared__ __align__(16) uint8_t st0[L::STAGE], st1[L::STAGE], st2[L::STAGE],
+        st3[L::STAGE];
+    // a unit's scale bytes: [NW][64 lanes][16 B], lane li (ls = 0) holding
+    // row / token li's 16 (the other lanes load copies)
+    __shared__ __align__(16) uint8_t sca[NW * 1024], scb[NW * 1024];
+    auto stage = [&] __device__(auto tag) -> uint8_t * {
+        constexpr int k = decltype(tag)::value;
+        if constexpr (k == 0)
+            return st0;
+        else if constexpr (k == 1)
+            return st1;
+        else if constexpr (k == 2)
+            return st2;
+        else
+            return st3;
+    };
+    const int C = a.cols, R = a.rows;
+    const int gpr = C / 32;
+    const int nunits = C / 512;
+    const int nsteps = nunits * A8T_NS;
+    const int nch = (a.b + 16 * NC - 1) / (16 * NC);
+    const int lid = xcd_logical(blockIdx.x, gridDim.x);
+    const int ch = lid % nch; // token chunk fastest: a row block's chunks share an XCD
+    const int rb = lid / nch;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, ls = lane >> 4;
+    const int t0 = ch * 16 * NC;
+    const int ntok = min(16 * NC, a.b - t0);
+    const int row0 = rb * (NW * 16);
+    const int64_t code_bytes = (int64_t)R * (C / 2);
+
+    // ---- per-lane load sources (rows past the end read row R - 1, tokens
+    // past the chunk its last token: never stored, and an MFMA output element
+    // depends on its own row and column only)
+    const int r = min(row0 + wave * 16 + li, R - 1);
+    const uint8_t *csrc = a.w + (int64_t)r * (C / 2) + ls * 16; // group ls of the step
+    const uint8_t *asrc = a.w + code_bytes + (int64_t)r * gpr;  // 16 scale bytes per unit
+    const uint8_t *xsrc[L::XL];
+#pragma unroll
+    for (int i = 0; i < L::XL; ++i) {
+        const int pos = (wave * L::XL + i) * 64 + lane; // slab position (16-byte chunks)
+        const int t = pos >> 3, k = (pos & 7) ^ (t & 7);
+        xsrc[i] = a.xq + (int64_t)(t0 + min(t, ntok - 1)) * C + k * 16;
+    }
+    const uint8_t *bsrc = a.xs + (int64_t)(t0 + min((wave % NC) * 16 + li, ntok - 1)) * gpr;
+    auto issue = [&] __device__(auto tag, int s) {
+        uint8_t *S = stage(tag);
+        lds_dma16(csrc + (int64_t)s * 64, S + L::CODES + wave * 1024);
+#pragma unroll
+        for (int i = 0; i < L::XL; ++i)
+            lds_dma16(xsrc[i] + (int64_t)s * 128, S + L::SLAB + (wave * L::XL + i) * 1024);
+        if constexpr (decltype(tag)::value == 0) { // a unit's first step: its scales
+            lds_dma16(asrc + (s / A8T_NS) * 16, sca + wave * 1024);
+            lds_dma16(bsrc + (s / A8T_NS) * 16, scb + wave * 1024);
+        }
+    };
+
+    f32x4 acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // prologue: steps 0 .. 2 in flight
+    issue(IntTag8<0>{}, 0);
+    issue(IntTag8<1>{}, 1);
+    issue(IntTag8<2>{}, 2);
+    u32x4 usa, usb[NC]; // the unit's scale bytes: word j = step j, byte ls = group ls
+    for (int un = 0; un < nunits; ++un) {
+        auto step = [&] __device__(auto jt) {
+            constexpr int j = decltype(jt)::value;
+            const int s = un * A8T_NS + j;
+            // stage j (step s) has landed for every wave; stage j - 1 is free
+            // (this wave's reads of it are done before the barrier).  Loads
+            // issued after stage j's: two steps' worth, plus the two scale
+            // loads of a unit's first step when that is one of them (j = 2, 3)
+            wait_vmcnt<(A8T_NS - 2) * L::GN + (j >= 2 ? 2 : 0)>();
+            wait_lgkm0();
+            raw_barrier();
+            issue(IntTag8<(j + 3) % A8T_NS>{}, min(s + 3, nsteps - 1));
+            if constexpr (j == 0) { // this unit's scales, before they are refilled
+                usa = *reinterpret_cast<const u32x4 *>(sca + wave * 1024 + li * 16);
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    usb[c] = *reinterpret_cast<const u32x4 *>(scb + c * 1024 + li * 16);
+            }
+            const uint8_t *S = stage(IntTag8<j>{});
+            const u32x4 av =
+                *reinterpret_cast<const u32x4 *>(S + L::CODES + wave * 1024 + lane * 16);
+            const i32x8 A = {(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0};
+            const int sa = (int)((usa[j] >> (8 * ls)) & 0xFFu); // row li, group ls
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int t = c * 16 + li;
+                const uint8_t *row = S + L::SLAB + t * 128;
+                const u32x4 lo = *reinterpret_cast<const u32x4 *>(row + ((ls ^ (t & 7)) * 16));
+                const u32x4 hi =
+                    *reinterpret_cast<const u32x4 *>(row + (((4 + ls) ^ (t & 7)) * 16));
+                const i32x8 B = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                const int sb = (int)((usb[c][j] >> (8 * ls)) & 0xFFu); // token t, block ls
+                acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    A, B, acc[c], 4 /* A: FP4 E2M1 */, 0 /* B: FP8 E4M3 */, 0, sa, 0, sb);
+            }
+        };
+        step(IntTag8<0>{});
+        step(IntTag8<1>{});
+        step(IntTag8<2>{});
+        step(IntTag8<3>{});
+    }
+    // the last steps' (clamped, unused) loads land before the workgroup ends
+    wait_vmcnt<0>();
+
+    // D: lane (li, ls) holds rows 4 ls .. 4 ls + 3 of token column li
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int t = t0 + c * 16 + li;
+        if (t >= a.b)
+            continue;
+        const int rbase = row0 + wave * 16 + 4 * ls;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = rbase + i;
+            if (rr >= R)
+                continue;
+            if (a.y_bf16)
+                reinterpret_cast<uint16_t *>(a.y)[(int64_t)t * R + rr] =
+                    f32_to_bf16_bits(acc[c][i]);
+            else
+                reinterpret_cast<float *>(a.y)[(int64_t)t * R + rr] = acc[c][i];
+        }
+    }
+}
+
 } // namespace
 
 hipError_t mxfp8_quantize_launch(const void *x, bool xbf, int64_t b, int64_t cols, uint8_t *q,
                                  uint8_t *s, hipStream_t stream)
 {
     const int64_t blocks = b * (cols / 32);
-    const unsigned grid = (unsigned)((blocks + 255) / 256);
+    const unsigned grid = (unsigned)((blocks * 8 + 255) / 256);
     if (xbf)
         hipLaunchKernelGGL(mxfp8_quantize_kernel<true>, dim3(grid), dim3(256), 0, stream, x,
-                           blocks, (int)(cols / 32), q, s);
+                           blocks, q, s);
     else
         hipLaunchKernelGGL(mxfp8_quantize_kernel<false>, dim3(grid), dim3(256), 0, stream, x,
-                           blocks, (int)(cols / 32), q, s);
+                           blocks, q, s);
     return hipGetLastError();
 }
 
@@ -280,6 +451,16 @@ hipError_t gemm_a8_launch(const A8Args &a, hipStream_t stream)
     // when the chunks of a row block run together)
     const int nc = a.b > 32 ? 4 : (a.b > 16 ? 2 : 1);
     const int64_t nch = (a.b + 16 * nc - 1) / (16 * nc);
+    if (nc >= 2 && a.cols % 512 == 0) {
+        // tiled: 64-row workgroups sharing one LDS copy of the activations
+        const int64_t nrb = (a.rows + 63) / 64;
+        const dim3 grid((unsigned)(nrb * nch)), block(4 * 64);
+        if (nc == 4)
+            hipLaunchKernelGGL((gemm_a8_tiled_kernel<4, 4>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemm_a8_tiled_kernel<4, 2>), grid, block, 0, stream, a);
+        return hipGetLastError();
+    }
     const int64_t nrb = (a.rows + a8_rows_per_wg() - 1) / a8_rows_per_wg();
     const dim3 grid((unsigned)(nrb * nch)), block(A8_NWK * 64);
     if (nc == 4)

@@ -59,41 +59,6 @@ __device__ __forceinline__ int64_t t_token_row(const SkinnyArgs &a, int slot0, i
     return slot0 + t;
 }
 
-// s_waitcnt with vmcnt(n) and the other counters left alone (gfx9 layout).
-template <int N> __device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Direct global -> LDS loads: `bytes` (16 or 4) per lane, lane l's bytes to
-// lds + l * bytes (lds is wave-uniform).  Kept in plain device functions: the
-// kernel templates' host pass must not see the builtin.
-__device__ __forceinline__ void lds_dma16(const void *g, void *lds)
-{
-    __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void *g, void *lds)
-{
-    __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
-}
-
-// s_waitcnt lgkmcnt(0) with the other counters left alone: this wave's LDS
-// writes are done.
-__device__ __forceinline__ void wait_lgkm0()
-{
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
-}
-
-// Workgroup barrier without a memory fence (a fence would wait for every
-// load in flight); the compiler barriers keep LDS accesses on their side.
-__device__ __forceinline__ void raw_barrier()
-{
-    __asm__ __volatile__("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ __volatile__("" ::: "memory");
-}
-
 } // namespace
 
 template <int NW, int RT, int NC, bool XBF, int MODE, bool PT>

@@ -78,6 +78,18 @@ def test_quantize_bit_exact(m, orc, xdt):
     assert np.array_equal(host(q), qo)
 
 
+def test_quantize_partial_workgroup(m, orc):
+    """21 blocks: the launch's last workgroup is partly past the end."""
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((7, 96)) * 3.0).astype(np.float32)
+    x[2, 33] = np.nan
+    q, s = m.mxfp8_quantize(dev(x))
+    torch.cuda.synchronize()
+    qo, so = orc.mxfp8_quantize(x)
+    assert np.array_equal(host(s), so)
+    assert np.array_equal(host(q), qo)
+
+
 def crafted(m, rows_w, x, rows=16, cols=128):
     """Run the product on crafted weights: rows_w maps (row, col) to
     (code, scale byte of that group); every other code is 0 and every
@@ -162,7 +174,9 @@ def check(m, orc, rows, cols, b, seed, xdt="f32", y_dtype=torch.float32):
 
 @pytest.mark.parametrize("rows,cols,b", [(4096, 4096, 1), (4096, 4096, 16), (4096, 4096, 64),
                                          (14336, 4096, 40), (70, 512, 3), (300, 2304, 17),
-                                         (1000, 128, 100), (12300, 1024, 64)])
+                                         (1000, 128, 100), (12300, 1024, 64),
+                                         (130, 256, 30), (200, 1536, 20), (130, 512, 70),
+                                         (300, 2048, 24)])
 def test_parity_at_the_contract(m, orc, rows, cols, b):
     check(m, orc, rows, cols, b, rows + cols + b)
 
