@@ -96,11 +96,20 @@ constexpr int TILED_NC = 4;
 constexpr int TILED_MIN_TOKENS = 8;
 constexpr int TILED_MIN_WGS = 192; // GEMM: tiled only with ~one workgroup per CU
 constexpr int TILED_FILL_WGS = 256; // GEMM: one workgroup per CU of MI355X
+// Expert bank on the tiled path: the down products of experts with at most
+// this many pairs run on the skinny kernel, one item each (measured, 256
+// experts of 7168 x 2048, bf16, every expert with c pairs, whole layer on
+// the 4-token skinny kernels against tiled: c = 1, 2, 4 in 1050, 1036,
+// 1108 us against 1273, 1275, 1302 us; c = 8, two 4-token items, 1830 us
+// against 1340 us.  In the 256-expert prefill layer, 99 such experts: down
+// 552 -> 378 + 148 us; their gate/up on the skinny kernel too, 992 -> 672 +
+// 328 us, so gate/up stays tiled).
+constexpr int COLD_MAX = 4;
 
 // Workspace layout of the expert bank.
 struct MoeLayout {
-    size_t offsets, pair_of_slot, slot_of_pair, token_of_slot, work, n_work, h, y, ids_aug, w_aug,
-        total;
+    size_t offsets, pair_of_slot, slot_of_pair, token_of_slot, work, n_work, work_cold,
+        n_work_cold, work_hot, n_work_hot, h, y, ids_aug, w_aug, total;
 };
 
 MoeLayout moe_layout(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t hidden,
@@ -120,6 +129,14 @@ MoeLayout moe_layout(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t
     L.work = o;
     o += align256((size_t)P * 16); // at most one item per pair
     L.n_work = o;
+    o += 256;
+    L.work_cold = o; // one item per expert with few pairs (tiled path)
+    o += align256((size_t)(n_experts < P ? n_experts : P) * 16);
+    L.n_work_cold = o;
+    o += 256;
+    L.work_hot = o; // the other experts' items (tiled path)
+    o += align256((size_t)P * 16);
+    L.n_work_hot = o;
     o += 256;
     L.h = o;
     o += align256((size_t)P * inter * (x_dtype == MXFP4_BF16 ? 2 : 4));
@@ -272,6 +289,23 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
     if (tpc < 1)
         return fail(MXFP4_EINVAL, "hidden/inter too large for the on-chip operand buffers");
     const int max_work = mx::group_max_work(P, (int)n_experts, tpc);
+    // tiled path: the down products of the experts with at most cold_max
+    // pairs, one item each, go to the skinny kernel (their own work list, at
+    // most min(E, P) items; the tiled down kernel takes the other experts'
+    // list, the tiled gate/up kernel every item, experts ascending: placing
+    // the few-pair experts' items last cost 8 us of 992 in the 256-expert
+    // prefill gate/up)
+    int cold_max = 0;
+    if (tiled) {
+        cold_max = mx::skinny_pick_tpc(mx::MODE_DOWN, xbf, (int)inter, COLD_MAX);
+        if (cold_max > COLD_MAX)
+            cold_max = COLD_MAX;
+    }
+    const int max_cold = (int)(n_experts < P ? n_experts : P);
+    int32_t *work_cold = reinterpret_cast<int32_t *>(ws + L.work_cold);
+    int32_t *n_work_cold = reinterpret_cast<int32_t *>(ws + L.n_work_cold);
+    int32_t *work_hot = reinterpret_cast<int32_t *>(ws + L.work_hot);
+    int32_t *n_work_hot = reinterpret_cast<int32_t *>(ws + L.n_work_hot);
 
     mx::GroupArgs g;
     g.ids = topk_ids;
@@ -285,6 +319,11 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
     g.token_of_slot = tos;
     g.work = work;
     g.n_work = n_work;
+    g.cold_max = cold_max;
+    g.work_hot = cold_max ? work_hot : nullptr;
+    g.n_work_hot = cold_max ? n_work_hot : nullptr;
+    g.work_cold = cold_max ? work_cold : nullptr;
+    g.n_work_cold = cold_max ? n_work_cold : nullptr;
     // Decode-sized routing (at most 64 pairs) into the split-K gate/up
     // kernel: it groups the routing itself (every workgroup ranks the pairs
     // with one wave; workgroup 0 writes the tables the down and combine
@@ -349,6 +388,18 @@ int moe_run(const void *gate, const void *up, const void *down, int64_t n_expert
         a.work = work;
         a.n_work = n_work;
         if (tiled) {
+            if (cold_max) {
+                mx::SkinnyArgs ac = a;
+                ac.nch = max_cold;
+                ac.work = work_cold;
+                ac.n_work = n_work_cold;
+                const mx::SkinnyShape sh = mx::skinny_shape(mx::MODE_DOWN, xbf, (int)hidden,
+                                                            (int)inter, cold_max, max_cold);
+                TRY(launched(mx::skinny_launch(mx::MODE_DOWN, xbf, sh, ac, st),
+                             "down (few-pair experts)"));
+                a.work = work_hot;
+                a.n_work = n_work_hot;
+            }
             TRY(launched(mx::tiled_launch(mx::MODE_DOWN, xbf, TILED_NW_MOE, TILED_RT_DOWN,
                                           TILED_NC, a, st),
                          "down"));

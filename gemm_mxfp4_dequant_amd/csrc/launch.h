@@ -108,6 +108,15 @@ struct GroupArgs {
     int32_t *token_of_slot; // [P] (may be null)
     int32_t *work;          // [max_work][4] (may be null)
     int32_t *n_work;        // [1] (may be null)
+    // 0, or: besides work (every item, experts ascending), the items of the
+    // experts with 1..cold_max pairs (one each) also go to work_cold
+    // [min(E, P)][4] and those of the other experts to work_hot [max_work][4]
+    // (counts in n_work_cold / n_work_hot [1])
+    int cold_max;
+    int32_t *work_hot;
+    int32_t *n_work_hot;
+    int32_t *work_cold;
+    int32_t *n_work_cold;
 };
 hipError_t group_launch(const GroupArgs &g, hipStream_t stream);
 int group_max_work(int n_pairs, int n_experts, int tpc);

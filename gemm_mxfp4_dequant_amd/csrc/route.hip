@@ -57,17 +57,58 @@ __device__ __forceinline__ int wave_inclusive_scan(int v)
     return v;
 }
 
+// Inclusive scans over the experts (E <= GT, expert = thread) of the pair
+// counts n, the work items ceil(n / tpc) and the cold experts (1 <= n <=
+// cold_max): shuffle scans within waves, then the wave totals.  scan
+// [3][GT], wsum [3][GT / 64] in LDS.
+__device__ void scan_experts(const GroupArgs &g, int n, int32_t *scan, int32_t *wsum)
+{
+    const int tid = threadIdx.x, wave = tid >> 6;
+    int v[3] = {n, (n + g.tpc - 1) / g.tpc, (n > 0 && n <= g.cold_max) ? 1 : 0};
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        v[i] = wave_inclusive_scan(v[i]);
+        if ((tid & 63) == 63)
+            wsum[i * (GT / 64) + wave] = v[i];
+    }
+    __syncthreads();
+    for (int w = 0; w < wave; ++w)
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            v[i] += wsum[i * (GT / 64) + w];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        scan[i * GT + tid] = v[i];
+    __syncthreads();
+}
+
+// The work items {expert, first slot, pairs, 0} of expert e (first slot s0,
+// n pairs), up to tpc pairs each, in work from position item0; with the
+// split on, also in work_cold at cold_idx (a cold expert: one item) or in
+// work_hot from position hot0.
+__device__ void write_items(const GroupArgs &g, int e, int s0, int n, int item0, int hot0,
+                            int cold_idx)
+{
+    const bool cold = n > 0 && n <= g.cold_max;
+    for (int c = 0; c * g.tpc < n; ++c) {
+        const int4 wk = make_int4(e, s0 + c * g.tpc, min(g.tpc, n - c * g.tpc), 0);
+        reinterpret_cast<int4 *>(g.work)[item0 + c] = wk;
+        if (cold)
+            reinterpret_cast<int4 *>(g.work_cold)[cold_idx] = wk;
+        else if (g.cold_max)
+            reinterpret_cast<int4 *>(g.work_hot)[hot0 + c] = wk;
+    }
+}
+
 __global__ __launch_bounds__(GT) void group_kernel(GroupArgs g, int nch)
 {
     extern __shared__ __align__(16) int32_t lds[];
     const int E = g.n_experts, P = g.n_pairs, tid = threadIdx.x;
     int32_t *cnt = lds;                 // [nch][E]
     int32_t *tot = cnt + nch * E;       // [E]
-    int32_t *scan_a = tot + E;          // [GT] offsets scan
-    int32_t *scan_b = scan_a + GT;      // [GT] work-item scan
-    int32_t *wsum_a = scan_b + GT;      // [GT / 64] wave totals
-    int32_t *wsum_b = wsum_a + GT / 64;
-    int32_t *sids = wsum_b + GT / 64;   // [P] when P <= IDS_IN_LDS
+    int32_t *scan = tot + E;            // [3][GT] scans over experts
+    int32_t *wsum = scan + 3 * GT;      // [3][GT / 64] wave totals
+    int32_t *sids = wsum + 3 * (GT / 64); // [P] when P <= IDS_IN_LDS
     const bool ids_lds = P <= IDS_IN_LDS;
     const int cs = (P + nch - 1) / nch;
 
@@ -100,36 +141,22 @@ __global__ __launch_bounds__(GT) void group_kernel(GroupArgs g, int nch)
         tot[e] = run;
     }
     __syncthreads();
-    // 3. inclusive scans over experts (E <= GT) of counts and work items:
-    //    shuffle scans within waves, then the wave totals
-    {
-        const int n = tid < E ? tot[tid] : 0;
-        int a = wave_inclusive_scan(n);
-        int b = wave_inclusive_scan((n + g.tpc - 1) / g.tpc);
-        const int wave = tid >> 6;
-        if ((tid & 63) == 63) {
-            wsum_a[wave] = a;
-            wsum_b[wave] = b;
-        }
-        __syncthreads();
-        for (int w = 0; w < wave; ++w) {
-            a += wsum_a[w];
-            b += wsum_b[w];
-        }
-        scan_a[tid] = a;
-        scan_b[tid] = b;
-        __syncthreads();
-    }
-    // offsets (exclusive) and the total
+    // 3. inclusive scans over experts of counts and work items
+    scan_experts(g, tid < E ? tot[tid] : 0, scan, wsum);
+    // offsets (exclusive) and the totals
     if (tid < E) {
-        const int excl = scan_a[tid] - tot[tid];
+        const int excl = scan[tid] - tot[tid];
         g.offsets[tid] = excl;
         tot[tid] = excl; // reuse: start slot of expert tid
     }
     if (tid == 0) {
-        g.offsets[E] = scan_a[E - 1];
+        g.offsets[E] = scan[E - 1];
         if (g.n_work)
-            *g.n_work = scan_b[E - 1];
+            *g.n_work = scan[GT + E - 1];
+        if (g.n_work_hot)
+            *g.n_work_hot = scan[GT + E - 1] - scan[2 * GT + E - 1];
+        if (g.n_work_cold)
+            *g.n_work_cold = scan[2 * GT + E - 1];
     }
     __syncthreads();
     // 4. ordered scatter
@@ -150,16 +177,10 @@ __global__ __launch_bounds__(GT) void group_kernel(GroupArgs g, int nch)
     }
     // 5. work items {expert, first slot, tokens, 0}
     if (g.work && tid < E) {
-        const int n = scan_a[tid] - tot[tid];
-        const int first_item = scan_b[tid] - (n + g.tpc - 1) / g.tpc;
-        for (int c = 0; c * g.tpc < n; ++c) {
-            int4 wk;
-            wk.x = tid;
-            wk.y = tot[tid] + c * g.tpc;
-            wk.z = min(g.tpc, n - c * g.tpc);
-            wk.w = 0;
-            reinterpret_cast<int4 *>(g.work)[first_item + c] = wk;
-        }
+        const int n = scan[tid] - tot[tid];
+        const int item0 = scan[GT + tid] - (n + g.tpc - 1) / g.tpc;
+        const int cold_before = scan[2 * GT + tid] - (n > 0 && n <= g.cold_max ? 1 : 0);
+        write_items(g, tid, tot[tid], n, item0, item0 - cold_before, scan[2 * GT + tid] - 1);
     }
 }
 
@@ -182,10 +203,8 @@ __global__ __launch_bounds__(GT) void group_tiles_kernel(GroupArgs g, int ntiles
     const int lane = tid & 63, wave = tid >> 6;
     int32_t *hist = lds;                 // [ntiles][E]: counts, then prefix over tiles
     int32_t *tot = hist + ntiles * E;    // [E]
-    int32_t *scan_a = tot + E;           // [GT] offsets scan
-    int32_t *scan_b = scan_a + GT;       // [GT] work-item scan
-    int32_t *wsum_a = scan_b + GT;       // [GT / 64] wave totals
-    int32_t *wsum_b = wsum_a + GT / 64;
+    int32_t *scan = tot + E;             // [3][GT] scans over experts
+    int32_t *wsum = scan + 3 * GT;       // [3][GT / 64] wave totals
 
     for (int i = tid; i < ntiles * E; i += GT)
         hist[i] = 0;
@@ -229,33 +248,21 @@ __global__ __launch_bounds__(GT) void group_tiles_kernel(GroupArgs g, int ntiles
         tot[e] = run;
     }
     __syncthreads();
-    // 3. inclusive scans over experts (E <= GT) of counts and work items
-    {
-        const int n = tid < E ? tot[tid] : 0;
-        int a = wave_inclusive_scan(n);
-        int b = wave_inclusive_scan((n + g.tpc - 1) / g.tpc);
-        if (lane == 63) {
-            wsum_a[wave] = a;
-            wsum_b[wave] = b;
-        }
-        __syncthreads();
-        for (int w = 0; w < wave; ++w) {
-            a += wsum_a[w];
-            b += wsum_b[w];
-        }
-        scan_a[tid] = a;
-        scan_b[tid] = b;
-        __syncthreads();
-    }
+    // 3. inclusive scans over experts of counts and work items
+    scan_experts(g, tid < E ? tot[tid] : 0, scan, wsum);
     if (tid < E) {
-        const int excl = scan_a[tid] - tot[tid];
+        const int excl = scan[tid] - tot[tid];
         g.offsets[tid] = excl;
         tot[tid] = excl; // reuse: start slot of expert tid
     }
     if (tid == 0) {
-        g.offsets[E] = scan_a[E - 1];
+        g.offsets[E] = scan[E - 1];
         if (g.n_work)
-            *g.n_work = scan_b[E - 1];
+            *g.n_work = scan[GT + E - 1];
+        if (g.n_work_hot)
+            *g.n_work_hot = scan[GT + E - 1] - scan[2 * GT + E - 1];
+        if (g.n_work_cold)
+            *g.n_work_cold = scan[2 * GT + E - 1];
     }
     __syncthreads();
     // 4. scatter, one pair per lane and tile
@@ -278,16 +285,10 @@ __global__ __launch_bounds__(GT) void group_tiles_kernel(GroupArgs g, int ntiles
     }
     // 5. work items {expert, first slot, tokens, 0}
     if (g.work && tid < E) {
-        const int n = scan_a[tid] - tot[tid];
-        const int first_item = scan_b[tid] - (n + g.tpc - 1) / g.tpc;
-        for (int c = 0; c * g.tpc < n; ++c) {
-            int4 wk;
-            wk.x = tid;
-            wk.y = tot[tid] + c * g.tpc;
-            wk.z = min(g.tpc, n - c * g.tpc);
-            wk.w = 0;
-            reinterpret_cast<int4 *>(g.work)[first_item + c] = wk;
-        }
+        const int n = scan[tid] - tot[tid];
+        const int item0 = scan[GT + tid] - (n + g.tpc - 1) / g.tpc;
+        const int cold_before = scan[2 * GT + tid] - (n > 0 && n <= g.cold_max ? 1 : 0);
+        write_items(g, tid, tot[tid], n, item0, item0 - cold_before, scan[2 * GT + tid] - 1);
     }
 }
 
@@ -304,6 +305,7 @@ __global__ __launch_bounds__(64) void group_small_kernel(GroupArgs g, int ntiles
     int32_t *cnt = hist + ntiles * E; // [E] pairs per expert
     int32_t *start = cnt + E;         // [E] first slot
     int32_t *item0 = start + E;       // [E] first work item
+    int32_t *split = item0 + E;       // [E] cold item / first item among the hot
 
     for (int i = lane; i < ntiles * E; i += 64)
         hist[i] = 0;
@@ -343,25 +345,35 @@ __global__ __launch_bounds__(64) void group_small_kernel(GroupArgs g, int ntiles
         cnt[e] = run;
     }
     __syncthreads();
-    int carry_a = 0, carry_b = 0;
+    // item0[e]: the expert's first work item; split[e]: its cold item, or
+    // its first item among the other experts'
+    int carry_a = 0, carry_b = 0, carry_c = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
         const int e = e0 + lane;
         const int n = e < E ? cnt[e] : 0;
+        const bool cold = n > 0 && n <= g.cold_max;
         const int ni = (n + g.tpc - 1) / g.tpc;
         const int a = wave_inclusive_scan(n) + carry_a;
         const int b = wave_inclusive_scan(ni) + carry_b;
+        const int c = wave_inclusive_scan(cold ? 1 : 0) + carry_c;
         if (e < E) {
             start[e] = a - n;
             item0[e] = b - ni;
+            split[e] = cold ? c - 1 : (b - c) - ni;
             g.offsets[e] = a - n;
         }
         carry_a = __shfl(a, 63, 64);
         carry_b = __shfl(b, 63, 64);
+        carry_c = __shfl(c, 63, 64);
     }
     if (lane == 0) {
         g.offsets[E] = carry_a;
         if (g.n_work)
             *g.n_work = carry_b;
+        if (g.n_work_hot)
+            *g.n_work_hot = carry_b - carry_c;
+        if (g.n_work_cold)
+            *g.n_work_cold = carry_c;
     }
     __syncthreads();
 #pragma unroll
@@ -381,17 +393,8 @@ __global__ __launch_bounds__(64) void group_small_kernel(GroupArgs g, int ntiles
         }
     }
     if (g.work) {
-        for (int e = lane; e < E; e += 64) {
-            const int n = cnt[e];
-            for (int c = 0; c * g.tpc < n; ++c) {
-                int4 wk;
-                wk.x = e;
-                wk.y = start[e] + c * g.tpc;
-                wk.z = min(g.tpc, n - c * g.tpc);
-                wk.w = 0;
-                reinterpret_cast<int4 *>(g.work)[item0[e] + c] = wk;
-            }
-        }
+        for (int e = lane; e < E; e += 64)
+            write_items(g, e, start[e], cnt[e], item0[e], split[e], split[e]);
     }
 }
 
@@ -399,13 +402,13 @@ hipError_t group_launch(const GroupArgs &g, hipStream_t stream)
 {
     const int ntiles = (g.n_pairs + 63) / 64;
     if (ntiles <= SMALL_TILES) {
-        const size_t slds = ((size_t)ntiles * g.n_experts + 3 * (size_t)g.n_experts) * 4;
-        // at most (8 + 3) * 1024 * 4 = 44 KB
+        const size_t slds = ((size_t)ntiles * g.n_experts + 4 * (size_t)g.n_experts) * 4;
+        // at most (8 + 4) * 1024 * 4 = 48 KB
         hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(64), slds, stream, g, ntiles);
         return hipGetLastError();
     }
     const size_t tlds =
-        ((size_t)ntiles * g.n_experts + g.n_experts + 2 * GT + 2 * (GT / 64)) * 4;
+        ((size_t)ntiles * g.n_experts + g.n_experts + 3 * GT + 3 * (GT / 64)) * 4;
     if (ntiles <= (GT / 64) * TPW && tlds <= 128 * 1024) {
         static std::atomic<uint8_t> topted{0};
         if (tlds > 64 * 1024 && !topted.load(std::memory_order_acquire)) {
@@ -421,7 +424,7 @@ hipError_t group_launch(const GroupArgs &g, hipStream_t stream)
     }
 
     const int nch = group_chunks(g.n_pairs, g.n_experts);
-    size_t lds = ((size_t)nch * g.n_experts + g.n_experts + 2 * GT + 2 * (GT / 64)) * 4;
+    size_t lds = ((size_t)nch * g.n_experts + g.n_experts + 3 * GT + 3 * (GT / 64)) * 4;
     if (g.n_pairs <= IDS_IN_LDS)
         lds += (size_t)g.n_pairs * 4;
     static std::atomic<uint8_t> opted{0};

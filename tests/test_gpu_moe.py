@@ -217,6 +217,30 @@ def test_workload5_prefill_hot_experts(m, orc, prefill_case):
                dense=True)
 
 
+@pytest.mark.parametrize("xd", ["f32", "bf16"])
+def test_tiled_bank_with_few_pair_experts(m, orc, xd):
+    """Routing for the tiled path (160 tokens x 3 on 24 experts) with three
+    hot experts (~140 pairs each: three 64-token items), twenty experts with
+    1, 2, 3 or 4 pairs (their down products one item each on the skinny
+    kernel, their gate/up items after the others' in the tiled kernel), one
+    with 5 (just past that cut: tiled throughout) and two dropped pairs;
+    every pair and token is checked."""
+    E, H, I, T, K = 24, 1024, 512, 160, 3
+    c = inputs.moe_case(48, E, H, I, T, K, xd, "softmax", scale_lo=100, scale_hi=114)
+    ids = np.tile(np.arange(K, dtype=np.int32), (T, 1))
+    cold = [e for e in range(3, 23) for _ in range(1 + (e - 3) % 4)] + [23] * 5
+    toks = np.random.default_rng(48).choice(T, len(cold), replace=False)
+    for t, e in zip(toks, cold):
+        ids[t, t % K] = e            # at most one such expert per token
+    rest = np.setdiff1d(np.arange(T), toks)
+    ids[rest[0], 1] = -1
+    ids[rest[1], 2] = E + 5
+    c["ids"] = ids
+    cnt = np.bincount(ids[(ids >= 0) & (ids < E)], minlength=E)
+    assert cnt[:3].min() > 128 and sorted(set(cnt[3:23])) == [1, 2, 3, 4] and cnt[23] == 5
+    check_case(m, orc, c, E, H, I, xd == "bf16")
+
+
 def test_rerun_bitwise(m):
     E, H, I, T, K = 16, 1024, 512, 12, 4
     c = inputs.moe_case(44, E, H, I, T, K, "f32", "softmax", scale_lo=100, scale_hi=114)
