@@ -259,42 +259,56 @@ __global__ __launch_bounds__(A8_NWK * 64) void gemm_a8_kernel(A8Args a)
 
 // The same product on the tiled schedule (cols % 512 == 0): a workgroup of NW
 // waves owns NW 16-row tiles (one per wave) and NC tiles of 16 tokens, and
-// runs the whole K loop in 128-column steps through a ring of four LDS
-// stages filled by direct global -> LDS loads (three steps in flight).  Per
-// step each wave loads its rows' 16 code bytes per lane and its share of the
-// activation slab (16 NC tokens x 128 E4M3 bytes, stored with 16-byte chunk
-// k of token t at position k ^ (t & 7), so that the sixteen lanes reading
-// one B fragment spread over the banks); with the first step of each
-// 512-column unit it also loads the unit's 16 scale bytes of its rows and of
-// one token tile's tokens, which the waves copy to registers at that step.
-// Every wave issues the same loads, so "stage s has landed" is one constant
-// vmcnt wait, then one barrier per step.  Every wave reads the slab from
-// LDS, so each activation byte fetched serves 16 NW rows.  One fp32
-// accumulator per token tile, steps in ascending order.
-//   Measured at 14336 x 4096, b = 64 (bf16 activations, quantize
-// included): scale bytes once per unit instead of 4-byte loads of 16 rows'
-// (or tokens') scales every step, 23.8 -> 18.9 us.  Not kept: rings of six
-// or eight stages (+4 %, +7 %), and K in two parts over eight waves with the
-// parts' sums added through LDS (19.4 us; b = 256: 51.4 -> 59.5 us).
-constexpr int A8T_NS = 4; // ring stages = steps per 512-column unit
-
+// runs the whole K loop in 128-column steps (four per 512-column unit).
+//  * Activations: a ring of four LDS stages, one per step, filled by direct
+//    global -> LDS loads three steps ahead with the step's 16 NC tokens x
+//    128 E4M3 bytes (16-byte chunk k of token t at position k ^ (t & 7), so
+//    that the sixteen lanes reading one B fragment spread over the banks);
+//    with the first step of each unit also the unit's 16 scale bytes of the
+//    wave's rows and of one token tile's tokens, which the waves copy to
+//    registers at that step.
+//  * Weights: a unit's codes of the wave's 16 rows (4 KB) in one of two
+//    per-wave buffers (unit parity), loaded as four 1 KB chunks of 4 rows x
+//    256 contiguous bytes: lane L of chunk c takes row 4c + L / 16 and the
+//    16-byte piece (L & 15) ^ row of its unit slice (so the sixteen lanes
+//    reading one A fragment spread over the banks).  Chunks 0-1 of unit v
+//    travel with the stage of step 4v - 1, chunks 2-3 with that of step 4v.
+//    Whole lines per row and instruction: measured against 16 rows x 64 B
+//    per instruction in every step's stage, 14336 x 4096 b = 64 18.8 ->
+//    17.9 us, b = 256 51.4 -> 43.1 us, 4096 x 14336 b = 64 45.1 -> 39.8 us.
+// Per stage every wave issues the same loads (how many depends only on the
+// step's place in its unit), so "stage s has landed" is one constant vmcnt
+// wait per step, then one barrier.  Every wave reads the slab from LDS, so
+// each activation byte fetched serves 16 NW rows.  One fp32 accumulator per
+// token tile, steps in ascending order.
+//   Measured at 14336 x 4096, b = 64 (bf16 activations, quantize included),
+// before the unit code buffers: scale bytes once per unit instead of 4-byte
+// loads of 16 rows' (or tokens') scales every step, 23.8 -> 18.9 us.  Not
+// kept: rings of six or eight stages (+4 %, +7 %), and K in two parts over
+// eight waves with the parts' sums added through LDS (19.4 us; b = 256: 51.4
+// -> 59.5 us).
 template <int NW, int NC> struct A8TLayout {
     static_assert((2 * NC) % NW == 0 && NC <= NW, "slab and scale loads spread over the waves");
-    static constexpr int CODES = 0;        // [NW][64 lanes][16 B]
-    static constexpr int SLAB = NW * 1024; // [16 NC tokens][8 chunks][16 B]
-    static constexpr int STAGE = SLAB + NC * 16 * 128;
-    static constexpr int XL = 2 * NC / NW; // slab loads per wave
-    static constexpr int GN = 1 + XL;      // loads per wave per step (+2 with a unit's first)
+    static constexpr int STAGE = NC * 16 * 128; // [16 NC tokens][8 chunks][16 B]
+    static constexpr int XL = 2 * NC / NW;      // slab loads per wave and step
+    // loads issued with the stages of the next two steps, by the place j of
+    // the current step in its unit (stage of place 3: two code chunks; place
+    // 0: two code chunks and two scale loads)
+    static constexpr int ahead(int j)
+    {
+        return j == 0 ? 2 * XL : j == 1 ? 2 * XL + 2 : j == 2 ? 2 * XL + 6 : 2 * XL + 4;
+    }
 };
 
 template <int NW, int NC>
 __global__ __launch_bounds__(NW * 64) void gemm_a8_tiled_kernel(A8Args a)
 {
     using L = A8TLayout<NW, NC>;
-    // one variable per stage: the loads into one stage and the reads of
-    // another are known not to alias
+    // one variable per buffer: the loads into one and the reads of another
+    // are known not to alias
     __shared__ __align__(16) uint8_t st0[L::STAGE], st1[L::STAGE], st2[L::STAGE],
         st3[L::STAGE];
+    __shared__ __align__(16) uint8_t cb0[NW * 4096], cb1[NW * 4096];
     // a unit's scale bytes: [NW][64 lanes][16 B], lane li (ls = 0) holding
     // row / token li's 16 (the other lanes load copies)
     __shared__ __align__(16) uint8_t sca[NW * 1024], scb[NW * 1024];
@@ -309,10 +323,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_a8_tiled_kernel(A8Args a)
         else
             return st3;
     };
+    auto codebuf = [&] __device__(auto tag) -> uint8_t * {
+        if constexpr (decltype(tag)::value == 0)
+            return cb0;
+        else
+            return cb1;
+    };
     const int C = a.cols, R = a.rows;
     const int gpr = C / 32;
     const int nunits = C / 512;
-    const int nsteps = nunits * A8T_NS;
+    const int nsteps = nunits * 4;
     const int nch = (a.b + 16 * NC - 1) / (16 * NC);
     const int lid = xcd_logical(blockIdx.x, gridDim.x);
     const int ch = lid % nch; // token chunk fastest: a row block's chunks share an XCD
@@ -327,9 +347,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_a8_tiled_kernel(A8Args a)
     // ---- per-lane load sources (rows past the end read row R - 1, tokens
     // past the chunk its last token: never stored, and an MFMA output element
     // depends on its own row and column only)
+    const uint8_t *crow[4]; // code chunk c: this lane's row and swizzled piece
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int lr = 4 * c + (lane >> 4);
+        const int r = min(row0 + wave * 16 + lr, R - 1);
+        crow[c] = a.w + (int64_t)r * (C / 2) + ((lane & 15) ^ lr) * 16;
+    }
     const int r = min(row0 + wave * 16 + li, R - 1);
-    const uint8_t *csrc = a.w + (int64_t)r * (C / 2) + ls * 16; // group ls of the step
-    const uint8_t *asrc = a.w + code_bytes + (int64_t)r * gpr;  // 16 scale bytes per unit
+    const uint8_t *asrc = a.w + code_bytes + (int64_t)r * gpr; // 16 scale bytes per unit
     const uint8_t *xsrc[L::XL];
 #pragma unroll
     for (int i = 0; i < L::XL; ++i) {
@@ -338,15 +364,32 @@ __global__ __launch_bounds__(NW * 64) void gemm_a8_tiled_kernel(A8Args a)
         xsrc[i] = a.xq + (int64_t)(t0 + min(t, ntok - 1)) * C + k * 16;
     }
     const uint8_t *bsrc = a.xs + (int64_t)(t0 + min((wave % NC) * 16 + li, ntok - 1)) * gpr;
-    auto issue = [&] __device__(auto tag, int s) {
+    auto load_codes = [&] __device__(auto bt, int c, int v) {
+        lds_dma16(crow[c] + (int64_t)v * 256, codebuf(bt) + wave * 4096 + c * 1024);
+    };
+    // the loads that travel with step q's stage (q may run past the end:
+    // sources clamp to the last step / unit, whose data is then not read);
+    // bt: the code buffer of the unit they carry codes for
+    auto issue = [&] __device__(auto tag, auto bt, int q) {
+        constexpr int st = decltype(tag)::value;
         uint8_t *S = stage(tag);
-        lds_dma16(csrc + (int64_t)s * 64, S + L::CODES + wave * 1024);
+        const int qs = min(q, nsteps - 1);
+        if constexpr (st == 3) {
+            const int v = min((q + 1) / 4, nunits - 1);
+            load_codes(bt, 0, v);
+            load_codes(bt, 1, v);
+        }
+        if constexpr (st == 0) {
+            const int v = min(q / 4, nunits - 1);
+            load_codes(bt, 2, v);
+            load_codes(bt, 3, v);
+        }
 #pragma unroll
         for (int i = 0; i < L::XL; ++i)
-            lds_dma16(xsrc[i] + (int64_t)s * 128, S + L::SLAB + (wave * L::XL + i) * 1024);
-        if constexpr (decltype(tag)::value == 0) { // a unit's first step: its scales
-            lds_dma16(asrc + (s / A8T_NS) * 16, sca + wave * 1024);
-            lds_dma16(bsrc + (s / A8T_NS) * 16, scb + wave * 1024);
+            lds_dma16(xsrc[i] + (int64_t)qs * 128, S + (wave * L::XL + i) * 1024);
+        if constexpr (st == 0) { // a unit's first step: its scales
+            lds_dma16(asrc + (qs / 4) * 16, sca + wave * 1024);
+            lds_dma16(bsrc + (qs / 4) * 16, scb + wave * 1024);
         }
     };
 
@@ -355,53 +398,65 @@ __global__ __launch_bounds__(NW * 64) void gemm_a8_tiled_kernel(A8Args a)
     for (int c = 0; c < NC; ++c)
         acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: steps 0 .. 2 in flight
-    issue(IntTag8<0>{}, 0);
-    issue(IntTag8<1>{}, 1);
-    issue(IntTag8<2>{}, 2);
+    // prologue: unit 0's code chunks 0-1, then steps 0 .. 2 in flight
+    load_codes(IntTag8<0>{}, 0, 0);
+    load_codes(IntTag8<0>{}, 1, 0);
+    issue(IntTag8<0>{}, IntTag8<0>{}, 0);
+    issue(IntTag8<1>{}, IntTag8<0>{}, 1);
+    issue(IntTag8<2>{}, IntTag8<0>{}, 2);
     u32x4 usa, usb[NC]; // the unit's scale bytes: word j = step j, byte ls = group ls
-    for (int un = 0; un < nunits; ++un) {
-        auto step = [&] __device__(auto jt) {
-            constexpr int j = decltype(jt)::value;
-            const int s = un * A8T_NS + j;
-            // stage j (step s) has landed for every wave; stage j - 1 is free
-            // (this wave's reads of it are done before the barrier).  Loads
-            // issued after stage j's: two steps' worth, plus the two scale
-            // loads of a unit's first step when that is one of them (j = 2, 3)
-            wait_vmcnt<(A8T_NS - 2) * L::GN + (j >= 2 ? 2 : 0)>();
-            wait_lgkm0();
-            raw_barrier();
-            issue(IntTag8<(j + 3) % A8T_NS>{}, min(s + 3, nsteps - 1));
-            if constexpr (j == 0) { // this unit's scales, before they are refilled
-                usa = *reinterpret_cast<const u32x4 *>(sca + wave * 1024 + li * 16);
+    // step j of unit u, whose codes are in buffer bt
+    auto step = [&] __device__(auto jt, auto bt, int u) {
+        constexpr int j = decltype(jt)::value;
+        constexpr int b = decltype(bt)::value;
+        const int s = u * 4 + j;
+        // stage j (step s) and unit u's codes have landed for every wave;
+        // stage j - 1 is free (this wave's reads of it are done before the
+        // barrier), and so is the other code buffer from place 0 on
+        wait_vmcnt<L::ahead(j)>();
+        wait_lgkm0();
+        raw_barrier();
+        issue(IntTag8<(j + 3) % 4>{}, IntTag8<1 - b>{}, s + 3);
+        if constexpr (j == 0) { // this unit's scales, before they are refilled
+            usa = *reinterpret_cast<const u32x4 *>(sca + wave * 1024 + li * 16);
 #pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    usb[c] = *reinterpret_cast<const u32x4 *>(scb + c * 1024 + li * 16);
-            }
-            const uint8_t *S = stage(IntTag8<j>{});
-            const u32x4 av =
-                *reinterpret_cast<const u32x4 *>(S + L::CODES + wave * 1024 + lane * 16);
-            const i32x8 A = {(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0};
-            const int sa = (int)((usa[j] >> (8 * ls)) & 0xFFu); // row li, group ls
+            for (int c = 0; c < NC; ++c)
+                usb[c] = *reinterpret_cast<const u32x4 *>(scb + c * 1024 + li * 16);
+        }
+        // A: row li, 16-byte piece 4 j + ls of the unit slice
+        const int kp = 4 * j + ls;
+        const u32x4 av = *reinterpret_cast<const u32x4 *>(
+            codebuf(bt) + wave * 4096 + (li >> 2) * 1024 + ((li & 3) * 16 + (kp ^ li)) * 16);
+        const i32x8 A = {(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0};
+        const int sa = (int)((usa[j] >> (8 * ls)) & 0xFFu); // row li, group ls
+        const uint8_t *S = stage(IntTag8<j>{});
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int t = c * 16 + li;
-                const uint8_t *row = S + L::SLAB + t * 128;
-                const u32x4 lo = *reinterpret_cast<const u32x4 *>(row + ((ls ^ (t & 7)) * 16));
-                const u32x4 hi =
-                    *reinterpret_cast<const u32x4 *>(row + (((4 + ls) ^ (t & 7)) * 16));
-                const i32x8 B = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                const int sb = (int)((usb[c][j] >> (8 * ls)) & 0xFFu); // token t, block ls
-                acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    A, B, acc[c], 4 /* A: FP4 E2M1 */, 0 /* B: FP8 E4M3 */, 0, sa, 0, sb);
-            }
-        };
-        step(IntTag8<0>{});
-        step(IntTag8<1>{});
-        step(IntTag8<2>{});
-        step(IntTag8<3>{});
+        for (int c = 0; c < NC; ++c) {
+            const int t = c * 16 + li;
+            const uint8_t *row = S + t * 128;
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(row + ((ls ^ (t & 7)) * 16));
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(row + (((4 + ls) ^ (t & 7)) * 16));
+            const i32x8 B = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            const int sb = (int)((usb[c][j] >> (8 * ls)) & 0xFFu); // token t, block ls
+            acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                A, B, acc[c], 4 /* A: FP4 E2M1 */, 0 /* B: FP8 E4M3 */, 0, sa, 0, sb);
+        }
+    };
+    auto unit = [&] __device__(auto bt, int u) {
+        step(IntTag8<0>{}, bt, u);
+        step(IntTag8<1>{}, bt, u);
+        step(IntTag8<2>{}, bt, u);
+        step(IntTag8<3>{}, bt, u);
+    };
+    // units in pairs, so that each one's code buffer is known at compile time
+    int u = 0;
+    for (; u + 1 < nunits; u += 2) {
+        unit(IntTag8<0>{}, u);
+        unit(IntTag8<1>{}, u + 1);
     }
+    if (u < nunits)
+        unit(IntTag8<0>{}, u);
     // the last steps' (clamped, unused) loads land before the workgroup ends
     wait_vmcnt<0>();
 
