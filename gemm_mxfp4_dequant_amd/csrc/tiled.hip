@@ -73,13 +73,24 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     constexpr int RB = NW * RT * 16;            // output rows per workgroup
     constexpr int ROWB = TKS * ES;              // bytes of one token per step
     constexpr int ACT_BYTES = TPD * ROWB;       // activation slab per step (at most)
-    // stage layout: codes [NW][MT][1 KB] | slab
-    constexpr int ACT_OFF = NW * MT * 1024;
+    // Codes: expert bank, two steps per load into pair buffers (whole cache
+    // lines, see below); plain GEMM, one step per load with the step's
+    // stage (its grids hold about one workgroup per CU, where the pairs'
+    // shorter lead showed: 14336 x 4096 b = 16 / 32 fp32 17.6 / 20.5 ->
+    // 18.4 / 21.2 us, bf16 b = 64 19.3 -> 20.4 us)
+    constexpr bool PAIRS = MODE != MODE_GEMM;
+    // stage layout: [codes [NW][MT][1 KB] without pairs] | slab
+    constexpr int ACT_OFF = PAIRS ? 0 : NW * MT * 1024;
     constexpr int STAGE = ACT_OFF + ACT_BYTES;
+    constexpr int PBB = PAIRS ? NW * MT * 2048 : 16;
 
-    // one variable per stage: loads into one stage and reads of another are
-    // then known not to alias, and the compiler adds no waits of its own
+    // one variable per stage and per code buffer: loads into one and reads
+    // of another are then known not to alias, and the compiler adds no waits
+    // of its own
     __shared__ __align__(16) uint8_t st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+    // codes of a pair of steps (256 columns) by pair parity: [NW][MT][2][1 KB],
+    // 1 KB i of a tile holding rows 8i .. 8i + 7 x 128 bytes (see below)
+    __shared__ __align__(16) uint8_t pb0[PBB], pb1[PBB];
     // scale bytes of one 512-column unit: [NW][64 lanes][16 B], loaded with
     // stage 0 (the unit's first step) and read into registers at that step
     __shared__ __align__(16) uint8_t scs[NW * 1024];
@@ -96,6 +107,12 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
             return st2;
         else
             return st3;
+    };
+    auto pairbuf = [&] __device__(auto tag) -> uint8_t * {
+        if constexpr (decltype(tag)::value == 0)
+            return pb0;
+        else
+            return pb1;
     };
 
     const int C = a.cols;
@@ -149,11 +166,27 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     // ---- per-lane load sources (rows past the end read row R-1: never
     // stored, and MFMA output rows depend on their own A row only)
     auto lrow = [&] __device__(int rt) { return min(row0 + (wave * RT + rt) * 16 + li, R - 1); };
-    // codes: lane (li, ls) loads group ls of step s of row li of each tile
-    const uint8_t *csrc[MT];
+    // codes, two steps (128 bytes of a row: whole cache lines) per load:
+    // load i of a tile takes rows 8i .. 8i + 7, lane L row 8i + L / 8 and the
+    // 16-byte piece (L & 7) ^ ((row / 2) & 7) of the pair's 128 bytes, so
+    // that the sixteen lanes reading one A fragment (rows 0..15, one piece)
+    // spread over the banks.  Measured against 16 rows x 64 B per load and
+    // step: 256-expert prefill layer 1546 -> 1403 us in a timing copy.
+    // Without pairs, lane (li, ls) loads group ls of step s of row li.
+    const uint8_t *csrc[MT][2];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-        csrc[mt] = Am[mt / RT] + (int64_t)lrow(mt % RT) * (C / 2) + ls * 16;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if constexpr (PAIRS) {
+                const int lr = 8 * i + (lane >> 3);
+                const int r = min(row0 + (wave * RT + mt % RT) * 16 + lr, R - 1);
+                csrc[mt][i] =
+                    Am[mt / RT] + (int64_t)r * (C / 2) + ((lane & 7) ^ ((lr >> 1) & 7)) * 16;
+            } else {
+                csrc[mt][i] = Am[mt / RT] + (int64_t)lrow(mt % RT) * (C / 2) + ls * 16;
+            }
+        }
     // scales: lane (li, ls) loads the 16 scale bytes of a unit for row li of
     // tile ls % MT (lanes of a repeated tile load the same bytes)
     const int smt = ls % MT;
@@ -183,8 +216,6 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
         constexpr int SB = TN * ROWB;                 // slab bytes loaded per step
         constexpr int AIN = SB / (NW * 1024);         // slab loads per wave per step
         static_assert(SB % (NW * 1024) == 0 && AIN >= 1 && TN <= TPD, "slab loads");
-        constexpr int GN = MT + AIN;                  // loads per wave per step (+1 scale
-                                                      // load with stage 0)
 
         // slab: load i of this wave fills bytes [(wave * AIN + i) KB, +1 KB)
         // of the slab; the 16 bytes at slab offset o belong to token
@@ -198,11 +229,26 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
             const int64_t row = t_token_row<MODE>(a, slot0, min(t, ntok - 1));
             xsrc[i] = reinterpret_cast<const uint8_t *>(a.x) + (row * C) * ES + k * 16;
         }
-        auto issue = [&] __device__(auto tag, int s) {
-            uint8_t *S = stage(tag);
+        // the codes of pair q (steps 2q, 2q + 1; clamped to the last pair,
+        // whose data is then not read) into the buffer of its parity
+        auto issue_codes = [&] __device__(auto pbt, int q) {
+            uint8_t *P = pairbuf(pbt);
+            const int qc = min(q, nsteps / 2 - 1);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                lds_dma16(csrc[mt] + s * (TKS / 2), S + (wave * MT + mt) * 1024);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    lds_dma16(csrc[mt][i] + qc * TKS, P + (wave * MT + mt) * 2048 + i * 1024);
+        };
+        // step s's slab (and its codes without pairs; with a unit's first
+        // step the unit's scales)
+        auto issue = [&] __device__(auto tag, int s) {
+            uint8_t *S = stage(tag);
+            if constexpr (!PAIRS) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    lds_dma16(csrc[mt][0] + s * (TKS / 2), S + (wave * MT + mt) * 1024);
+            }
 #pragma unroll
             for (int i = 0; i < AIN; ++i)
                 lds_dma16(xsrc[i] + s * ROWB, S + ACT_OFF + (wave * AIN + i) * 1024);
@@ -210,8 +256,11 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
                 lds_dma16(ssrc + (s / 4) * 16, scs + wave * 1024);
         };
 
-        // prologue: the token gathers above have landed; steps 0..2 in flight
+        // prologue: the token gathers above have landed; pair 0's codes and
+        // steps 0..2 in flight
         wait_vmcnt<0>();
+        if constexpr (PAIRS)
+            issue_codes(IntTag<0>{}, 0);
         issue(IntTag<0>{}, 0);
         issue(IntTag<1>{}, min(1, nsteps - 1));
         issue(IntTag<2>{}, min(2, nsteps - 1));
@@ -221,16 +270,29 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
             auto step = [&] __device__(auto jt) {
                 constexpr int j = decltype(jt)::value;
                 const int s = un * TNS + j;
-                // stage j (step s) has landed for every wave; stage j - 1
-                // (step s - 1) is free.  Loads issued after stage j's: two
-                // steps' worth, plus the scale load of the stage-0 step when
-                // that is one of them (j = 2, 3).
+                // stage j (step s) and the codes of this step's pair have
+                // landed for every wave; stage j - 1 (step s - 1) is free, and
+                // at an even step so is the other pair buffer.  Issued at
+                // each step: at places 0 and 2 the next pair's codes (2 MT
+                // loads), then step s + 3's slab (AIN), plus the unit's
+                // scales at place 1; a pair's codes go out two steps before
+                // its first step, a slab three.  Loads issued after the last
+                // one this step needs:
+                // (without pairs: two steps' worth, MT + AIN each, plus the
+                // scale load of the stage-0 step when it is one of them)
+                constexpr int AHEAD = !PAIRS   ? 2 * (MT + AIN) + (j >= 2 ? 1 : 0)
+                                      : j == 0 ? 2 * AIN
+                                      : j == 1 ? 2 * MT + 2 * AIN
+                                      : j == 2 ? 2 * AIN + 1
+                                               : 2 * MT + 2 * AIN + 1;
                 // (this wave's LDS reads of the previous step, which was
                 // stage j - 1, the one refilled below, are done before the
                 // barrier: the barrier itself orders no memory)
-                wait_vmcnt<(TNS - 2) * GN + (j >= 2 ? 1 : 0)>();
+                wait_vmcnt<AHEAD>();
                 wait_lgkm0();
                 raw_barrier();
+                if constexpr (PAIRS && j % 2 == 0)
+                    issue_codes(IntTag<(j / 2 + 1) % 2>{}, s / 2 + 1);
                 issue(IntTag<(j + 3) % TNS>{}, min(s + 3, nsteps - 1));
 
                 const uint8_t *S = stage(IntTag<j>{});
@@ -265,12 +327,19 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
                         usc[mt] = *reinterpret_cast<const u32x4 *>(scs + wave * 1024 +
                                                                    (mt * 16 + li) * 16);
                 }
+                // A: row li, group ls of the step (with pairs: piece
+                // 4 (j % 2) + ls of the pair's 128 bytes of the row)
+                const uint8_t *CB = PAIRS ? pairbuf(IntTag<(j / 2) % 2>{}) : S;
+                const int kp = 4 * (j % 2) + ls;
+                const int aoff = PAIRS ? (li >> 3) * 1024 +
+                                             ((li & 7) * 8 + (kp ^ ((li >> 1) & 7))) * 16
+                                       : lane * 16;
+                constexpr int ASTR = PAIRS ? 2048 : 1024;
                 u32x4 cw[MT];
                 float scf[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    cw[mt] = *reinterpret_cast<const u32x4 *>(S + (wave * MT + mt) * 1024 +
-                                                              (ls * 16 + li) * 16);
+                    cw[mt] = *reinterpret_cast<const u32x4 *>(CB + (wave * MT + mt) * ASTR + aoff);
                     scf[mt] = e8m0_operand_of(usc[mt][j], ls);
                 }
 #pragma unroll
