@@ -102,8 +102,9 @@ constexpr int TILED_FILL_WGS = 256; // GEMM: one workgroup per CU of MI355X
 // the 4-token skinny kernels against tiled: c = 1, 2, 4 in 1050, 1036,
 // 1108 us against 1273, 1275, 1302 us; c = 8, two 4-token items, 1830 us
 // against 1340 us.  In the 256-expert prefill layer, 99 such experts: down
-// 552 -> 378 + 148 us; their gate/up on the skinny kernel too, 992 -> 672 +
-// 328 us, so gate/up stays tiled).
+// 552 -> 378 + 148 us with per-step code loads in the tiled kernels, 510 ->
+// 356 + 151 us with paired ones; their gate/up on the skinny kernel too,
+// 992 -> 672 + 328 us, so gate/up stays tiled).
 constexpr int COLD_MAX = 4;
 
 // Workspace layout of the expert bank.
