@@ -561,7 +561,24 @@ def main():
                                      "pct_peak": round(100 * s["touched"] / ms / 1e6 / 8000, 1),
                                      **spread_us(t, 10)}
         log(f"moe_prefill_e256: {extra['moe_prefill_e256']}")
-        del s, t
+        del t
+        # the same layer on the opt-in FP4 x FP8 bank (x and h quantized to
+        # MXFP8), on the same weights and routing
+        cfg = inputs.WORKLOADS[5]
+        E, H, I = cfg["n_experts"], cfg["hidden"], cfg["inter"]
+        ws8 = torch.empty(mx.moe_experts_mxfp4_a8_workspace_size(s["T"], cfg["top_k"], E, H, I),
+                          dtype=torch.uint8, device="cuda")
+        bk = s["bank"][0]
+        L = [lambda: mx.moe_experts_mxfp4_a8(bk[0], bk[1], bk[2], E, H, I, s["x"], s["ids"],
+                                             s["w"], out=s["out"], workspace=ws8)]
+        t = Timer(torch, L, args.eager, passes=4)
+        ms = t.time(8)
+        extra["moe_prefill_e256_a8"] = {"us_per_layer": round(ms * 1e3, 2),
+                                        "tok_per_s": round(s["T"] / (ms * 1e-3), 1),
+                                        "touched_GBps": round(s["touched"] / ms / 1e6, 1),
+                                        **spread_us(t, 10)}
+        log(f"moe_prefill_e256_a8: {extra['moe_prefill_e256_a8']}")
+        del s, t, L, ws8
         torch.cuda.empty_cache()
         # the same layer in V4.1 form: bf16 gate/up, SwiGLU limit 10, route
         # weight folded into h, plus a shared expert on every token

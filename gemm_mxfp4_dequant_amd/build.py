@@ -14,8 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libmxfp4.so")
-SOURCES = ["api.hip", "skinny.hip", "tiled.hip", "mx8.hip", "dequant.hip", "route.hip",
-           "router.hip", "probe.hip"]
+SOURCES = ["api.hip", "skinny.hip", "tiled.hip", "mx8.hip", "moe_a8.hip", "dequant.hip",
+           "route.hip", "router.hip", "probe.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

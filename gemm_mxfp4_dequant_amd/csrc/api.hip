@@ -151,6 +151,32 @@ MoeLayout moe_layout(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t
     return L;
 }
 
+// Workspace of the FP4 x FP8 expert bank: the plain bank's (h in fp32) and
+// the MXFP8 activations of x and h.
+struct MoeA8Layout {
+    MoeLayout L;
+    size_t xq, xs, hq, hs, total;
+};
+
+MoeA8Layout moe_a8_layout(int64_t n_tokens, int64_t top_k, int64_t n_experts, int64_t hidden,
+                          int64_t inter)
+{
+    const int64_t P = n_tokens * top_k;
+    MoeA8Layout A;
+    A.L = moe_layout(n_tokens, top_k, n_experts, hidden, inter, MXFP4_F32);
+    size_t o = A.L.total;
+    A.xq = o;
+    o += align256((size_t)n_tokens * hidden);
+    A.xs = o;
+    o += align256((size_t)n_tokens * (hidden / 32));
+    A.hq = o;
+    o += align256((size_t)P * inter);
+    A.hs = o;
+    o += align256((size_t)P * (inter / 32));
+    A.total = o;
+    return A;
+}
+
 // Expert-bank variants: the plain bank (route weight on the fp32 down
 // output) or the V4.1 bank (bf16 gate/up, SwiGLU limit, route weight folded
 // into the bf16 activation, slots summed unweighted, optional shared expert
@@ -710,6 +736,104 @@ int moe_experts_mxfp4(const void *gate, const void *up, const void *down, int64_
     return moe_run(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
                    topk_w, top_k, out, out_dtype, workspace, nullptr, nullptr, MoeMode{},
                    (hipStream_t)stream);
+}
+
+size_t moe_experts_mxfp4_a8_workspace_size(int64_t n_tokens, int64_t top_k, int64_t n_experts,
+                                           int64_t hidden, int64_t inter)
+{
+    if (n_tokens < 1 || top_k < 1 || n_experts < 1 || hidden < 512 || inter < 512 ||
+        hidden % 512 || inter % 512 || n_tokens > MXFP4_MAX_TOKENS ||
+        top_k > MXFP4_MAX_TOP_K || n_experts > MXFP4_MAX_EXPERTS || hidden > MXFP4_MAX_COLS ||
+        inter > MXFP4_MAX_COLS)
+        return 0;
+    return moe_a8_layout(n_tokens, top_k, n_experts, hidden, inter).total;
+}
+
+int moe_experts_mxfp4_a8(const void *gate, const void *up, const void *down, int64_t n_experts,
+                         int64_t hidden, int64_t inter, const void *x, int x_dtype,
+                         int64_t n_tokens, const int32_t *topk_ids, const float *topk_w,
+                         int64_t top_k, void *out, int out_dtype, void *workspace,
+                         size_t workspace_bytes, void *stream)
+{
+    clear_error();
+    // the shared checks (the workspace is checked below, against this
+    // entry point's own layout)
+    TRY(check_moe(gate, up, down, n_experts, hidden, inter, x, x_dtype, n_tokens, topk_ids,
+                  topk_w, top_k, out, out_dtype, true, NOALLOC_WS, 0));
+    if (hidden % 512 || inter % 512)
+        return fail(MXFP4_EINVAL,
+                    "hidden = %lld, inter = %lld: the FP4 x FP8 expert bank needs multiples "
+                    "of 512",
+                    (long long)hidden, (long long)inter);
+    TRY(check_buffer("workspace", workspace, 16));
+    const MoeA8Layout A = moe_a8_layout(n_tokens, top_k, n_experts, hidden, inter);
+    if (workspace_bytes < A.total)
+        return fail(MXFP4_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                    A.total);
+    const int P = (int)(n_tokens * top_k);
+    const int tpc = mx::moe_a8_tokens();
+    const int max_work = mx::group_max_work(P, (int)n_experts, tpc);
+    const int64_t rows_max = hidden > inter ? hidden : inter;
+    const int64_t nrb = (rows_max + mx::moe_a8_rows_per_wg() - 1) / mx::moe_a8_rows_per_wg();
+    if (nrb * max_work > ((int64_t)1 << 31) - 1)
+        return fail(MXFP4_EINVAL, "n_tokens * top_k * rows too large for one launch");
+    const hipStream_t st = (hipStream_t)stream;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const MoeLayout &L = A.L;
+    int32_t *slot = reinterpret_cast<int32_t *>(ws + L.slot_of_pair);
+    int32_t *tos = reinterpret_cast<int32_t *>(ws + L.token_of_slot);
+    int32_t *work = reinterpret_cast<int32_t *>(ws + L.work);
+    int32_t *n_work = reinterpret_cast<int32_t *>(ws + L.n_work);
+    float *h = reinterpret_cast<float *>(ws + L.h);
+    float *y = reinterpret_cast<float *>(ws + L.y);
+    uint8_t *xq = ws + A.xq, *xs = ws + A.xs, *hq = ws + A.hq, *hs = ws + A.hs;
+
+    TRY(launched(mx::mxfp8_quantize_launch(x, x_dtype == MXFP4_BF16, n_tokens, hidden, xq, xs,
+                                           st),
+                 "x quantize"));
+    mx::GroupArgs g = {};
+    g.ids = topk_ids;
+    g.n_pairs = P;
+    g.top_k = (int)top_k;
+    g.n_experts = (int)n_experts;
+    g.tpc = tpc;
+    g.offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+    g.pair_of_slot = reinterpret_cast<int32_t *>(ws + L.pair_of_slot);
+    g.slot_of_pair = slot;
+    g.token_of_slot = tos;
+    g.work = work;
+    g.n_work = n_work;
+    TRY(launched(mx::group_launch(g, st), "group"));
+    const int64_t tbytes = mxfp4_nbytes(inter, hidden);
+    mx::MoeA8Args a = {};
+    a.w0 = static_cast<const uint8_t *>(gate);
+    a.w1 = static_cast<const uint8_t *>(up);
+    a.expert_stride = tbytes;
+    a.rows = (int)inter;
+    a.cols = (int)hidden;
+    a.xq = xq;
+    a.xs = xs;
+    a.token_of_slot = tos;
+    a.work = work;
+    a.n_work = n_work;
+    a.max_work = max_work;
+    a.y = h;
+    TRY(launched(mx::moe_a8_launch(mx::MODE_GATEUP, a, st), "gate/up"));
+    // h of every slot (those of dropped pairs hold stale values: quantized,
+    // never read)
+    TRY(launched(mx::mxfp8_quantize_launch(h, false, P, inter, hq, hs, st), "h quantize"));
+    a.w0 = static_cast<const uint8_t *>(down);
+    a.w1 = nullptr;
+    a.rows = (int)hidden;
+    a.cols = (int)inter;
+    a.xq = hq;
+    a.xs = hs;
+    a.token_of_slot = nullptr;
+    a.y = y;
+    TRY(launched(mx::moe_a8_launch(mx::MODE_DOWN, a, st), "down"));
+    return launched(mx::combine_launch(y, slot, topk_w, (int)n_tokens, (int)top_k, (int)hidden,
+                                       out, out_dtype == MXFP4_BF16, st),
+                    "combine");
 }
 
 int mxfp4_device_address(const void *p, void **device_ptr)

@@ -94,6 +94,27 @@ hipError_t mxfp8_quantize_launch(const void *x, bool xbf, int64_t b, int64_t col
 hipError_t gemm_a8_launch(const A8Args &a, hipStream_t stream);
 int a8_rows_per_wg();
 
+// Expert bank on the block-scaled FP4 x FP8 product (moe_a8.hip), for work
+// items of up to moe_a8_tokens() tokens of one expert.  Activations MXFP8:
+// codes xq [rows of x][cols], scales xs [rows of x][cols / 32].  GATEUP:
+// x rows gathered by token_of_slot, y = h [slot][rows] = silu(g) u (fp32);
+// DOWN: x rows are slots, y [slot][rows] (fp32).  cols % 512 == 0.
+struct MoeA8Args {
+    const uint8_t *w0, *w1; // GATEUP: gate / up banks; DOWN: down bank
+    int64_t expert_stride;  // bytes between experts in a bank
+    int rows, cols;         // of one tensor
+    const uint8_t *xq, *xs;
+    const int *token_of_slot; // GATEUP
+    const int *work;          // int4 {expert, first slot, tokens, 0} per item
+    const int *n_work;        // number of items (device)
+    int max_work;             // bound on the items (grid)
+    float *y;
+};
+// grid = ceil(rows / moe_a8_rows_per_wg()) * max_work
+hipError_t moe_a8_launch(int mode, const MoeA8Args &a, hipStream_t stream);
+int moe_a8_rows_per_wg();
+int moe_a8_tokens();
+
 hipError_t dequant_launch(const uint8_t *w, int64_t rows, int64_t cols, void *out, bool bf16,
                           hipStream_t stream);
 

@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
                                           P]),
         "moe_experts_mxfp4_ptrs": (I, [P, P, P, I64, I64, I64, P, I, I64, P, P, I64, P, I, P,
                                        ctypes.c_size_t, P]),
+        "moe_experts_mxfp4_a8_workspace_size": (ctypes.c_size_t, [I64, I64, I64, I64, I64]),
+        "moe_experts_mxfp4_a8": (I, [P, P, P, I64, I64, I64, P, I, I64, P, P, I64, P, I, P,
+                                     ctypes.c_size_t, P]),
         "mxfp4_device_address": (I, [P, ctypes.POINTER(ctypes.c_void_p)]),
         "moe_experts_mxfp4_v41_workspace_size": (ctypes.c_size_t, [I64, I64, I64, I64, I64, I]),
         "moe_experts_mxfp4_v41": (I, [P, P, P, I64, I64, I64, P, I64, P, P, I64,
@@ -360,6 +363,33 @@ def moe_experts_mxfp4(gate, up, down, n_experts, hidden, inter, x, topk_ids, top
     _check(lib().moe_experts_mxfp4(_ptr(gate), _ptr(up), _ptr(down), n_experts, hidden, inter,
                                    _ptr(x), _dt(x), T, _ptr(topk_ids), _ptr(topk_w), K, _ptr(out),
                                    _dt(out), _ptr(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+def moe_experts_mxfp4_a8_workspace_size(n_tokens, top_k, n_experts, hidden, inter) -> int:
+    return int(lib().moe_experts_mxfp4_a8_workspace_size(n_tokens, top_k, n_experts, hidden,
+                                                         inter))
+
+
+def moe_experts_mxfp4_a8(gate, up, down, n_experts, hidden, inter, x, topk_ids, topk_w,
+                         out=None, out_dtype=torch.bfloat16, workspace=None, stream=None):
+    """Opt-in expert bank on the block-scaled FP4 x FP8 product (x and h
+    quantized to MXFP8; its own accuracy contract, see include/mxfp4.h)."""
+    _sizes(n_experts=n_experts)
+    d = _bank(gate, up, down, n_experts, hidden, inter)
+    T, K, _ = _routing(topk_ids, d, topk_w)
+    _req(x, "x", _ACT, T * hidden, d)
+    if out is None:
+        out = torch.empty((T, hidden), dtype=out_dtype, device=d)
+    _req(out, "out", _ACT, T * hidden, d)
+    need = moe_experts_mxfp4_a8_workspace_size(T, K, n_experts, hidden, inter)
+    if need <= 0:
+        raise ValueError(f"hidden = {hidden}, inter = {inter}: no FP4 x FP8 expert bank "
+                         "(multiples of 512 needed)")
+    ws, ws_bytes = _ws(workspace, need, d)
+    _check(lib().moe_experts_mxfp4_a8(_ptr(gate), _ptr(up), _ptr(down), n_experts, hidden,
+                                      inter, _ptr(x), _dt(x), T, _ptr(topk_ids), _ptr(topk_w), K,
+                                      _ptr(out), _dt(out), _ptr(ws), ws_bytes, _stream(stream)))
     return out
 
 

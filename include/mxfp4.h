@@ -165,6 +165,36 @@ int moe_route_group(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k, in
 int moe_route_topk(const float *logits, int64_t n_tokens, int64_t n_experts, int64_t top_k,
                    int32_t *topk_ids, float *topk_w, void *stream);
 
+/* Workspace bytes of moe_experts_mxfp4_a8 (0 on bad sizes: hidden and
+ * inter must be multiples of 512). */
+size_t moe_experts_mxfp4_a8_workspace_size(int64_t n_tokens, int64_t top_k, int64_t n_experts,
+                                           int64_t hidden, int64_t inter);
+
+/* Opt-in routed expert bank on the block-scaled FP4 x FP8 product, for
+ * dense prefill experts: the bank of moe_experts_mxfp4 with x quantized to
+ * MXFP8 (mxfp8_quantize) before gate/up, h = silu(g) * u computed in fp32
+ * and quantized to MXFP8 before down, and every expert product on
+ * v_mfma_scale_f32_16x16x128_f8f6f4 (weights as stored, no decode).
+ * Accuracy (its own contract, that of mxfp4_gemm_a8 for each product): each
+ * of g, u, y within 2^-7 of the sum of |w * a| over its terms of the exact
+ * product with its quantized activation a (xq for g and u, hq for y), then
+ * out[t] = sum_k topk_w[p] * y_p in slot order, fp32, rounded to out_dtype;
+ * against the unquantized x and h, the MXFP8 rounding adds up to 2^-4 of
+ * each element.  The same routing, grouping and combine as
+ * moe_experts_mxfp4 (ids outside [0, n_experts) drop the pair), items of up
+ * to 64 tokens per expert.  hidden % 512 == 0, inter % 512 == 0; other
+ * arguments, layout and errors as moe_experts_mxfp4; the workspace (device,
+ * 16-byte aligned, at least moe_experts_mxfp4_a8_workspace_size bytes) is
+ * scratch owned by the call until the stream reaches it.
+ * "cortiq-engine 0.8.77, src/qtensor/moe_fast.rs" (gate_up_block,
+ * down_block); "cortiq-engine 0.8.40, src/gpu_wgpu/mxfp4.rs" (module doc:
+ * the OCP MX formats). */
+int moe_experts_mxfp4_a8(const void *gate, const void *up, const void *down, int64_t n_experts,
+                         int64_t hidden, int64_t inter, const void *x, int x_dtype,
+                         int64_t n_tokens, const int32_t *topk_ids, const float *topk_w,
+                         int64_t top_k, void *out, int out_dtype, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /* Workspace bytes moe_experts_mxfp4 needs for these sizes (0 on bad sizes). */
 size_t moe_experts_mxfp4_workspace_size(int64_t n_tokens, int64_t top_k, int64_t n_experts,
                                         int64_t hidden, int64_t inter, int x_dtype);

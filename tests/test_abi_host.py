@@ -36,7 +36,7 @@ def m():
 
 def test_exports_every_declared_symbol(m):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     L = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(L, n), n
@@ -143,6 +143,33 @@ def test_moe_refusals(m):
     assert call(ids=FAKE + 2) == m.MXFP4_EALIGN
     assert call(xdt=5) == m.MXFP4_EINVAL
     assert args
+
+
+def test_moe_a8_refusals(m):
+    """The FP4 x FP8 expert bank sizes its own workspace (the plain bank's
+    with h in fp32, plus the MXFP8 codes and scales of x and h), needs hidden
+    and inter in multiples of 512, and refuses like the plain bank before
+    any launch."""
+    L = m.lib()
+    T, K, E, H, I = 512, 8, 256, 7168, 2048
+    ws = m.moe_experts_mxfp4_a8_workspace_size(T, K, E, H, I)
+    base = m.moe_experts_mxfp4_workspace_size(T, K, E, H, I, 0)
+    assert ws >= base + T * H + T * H // 32 + T * K * I + T * K * I // 32
+    assert m.moe_experts_mxfp4_a8_workspace_size(T, K, E, 7168 - 32, I) == 0
+    assert m.moe_experts_mxfp4_a8_workspace_size(T, K, E, H, 2048 + 256) == 0
+    assert m.moe_experts_mxfp4_a8_workspace_size(0, K, E, H, I) == 0
+
+    def call(E=E, H=H, I=I, K=K, ws_bytes=ws, wsp=FAKE, xdt=1):
+        return L.moe_experts_mxfp4_a8(FAKE, FAKE, FAKE, E, H, I, FAKE, xdt, T, FAKE, FAKE, K,
+                                      FAKE, 1, wsp, ws_bytes, None)
+
+    assert call(H=7168 - 32) == m.MXFP4_EINVAL      # hidden % 512
+    assert "512" in m.mxfp4_last_error()
+    assert call(I=2048 + 256) == m.MXFP4_EINVAL     # inter % 512
+    assert call(ws_bytes=ws - 1) == m.MXFP4_EWORKSPACE
+    assert call(wsp=FAKE + 4) == m.MXFP4_EALIGN
+    assert call(K=257) == m.MXFP4_EINVAL
+    assert call(xdt=7) == m.MXFP4_EINVAL
 
 
 def test_v41_refusals(m):
