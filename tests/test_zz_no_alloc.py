@@ -41,12 +41,22 @@ def no_alloc(m, d, E, H, I):
     return host(out)
 
 
-@pytest.mark.parametrize("xd", ["f32", "bf16"])
-def test_noalloc_equals_workspace_bank(m, orc, xd):
-    E, H, I = 16, 4096, 2048
-    big = inputs.moe_case(61, E, H, I, 8, 6, xd, "softmax", scale_lo=100, scale_hi=114)
+@pytest.mark.parametrize("xd,shape", [("f32", "decode"), ("bf16", "decode"), ("bf16", "tiled")])
+def test_noalloc_equals_workspace_bank(m, orc, xd, shape):
+    # decode: 48 pairs on 16 experts (split-K kernels, grouping inside
+    # gate/up); tiled: 192 Zipf-routed pairs (tiled kernels, with experts
+    # of at most four pairs on the skinny down kernel)
+    if shape == "decode":
+        E, H, I, T, K, routing, t_small = 16, 4096, 2048, 8, 6, "softmax", 3
+    else:
+        E, H, I, T, K, routing, t_small = 16, 1024, 512, 96, 2, "zipf", 40
+    big = inputs.moe_case(61, E, H, I, T, K, xd, routing, scale_lo=100, scale_hi=114)
+    if shape == "tiled":
+        cnt = np.bincount(big["ids"].reshape(-1), minlength=E)
+        assert cnt.max() > 16 and ((cnt > 0) & (cnt <= 4)).any(), cnt
     small = dict(big)
-    small["x"], small["ids"], small["w"] = big["x"][:3], big["ids"][:3], big["w"][:3]
+    small["x"], small["ids"], small["w"] = (big["x"][:t_small], big["ids"][:t_small],
+                                            big["w"][:t_small])
     db, ds = upload(big), upload(small)
     ref_b, ref_s = with_ws(m, db, E, H, I), with_ws(m, ds, E, H, I)
     got_b = no_alloc(m, db, E, H, I)
