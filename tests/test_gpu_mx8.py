@@ -106,6 +106,25 @@ def crafted(m, rows_w, x, rows=16, cols=128):
     return host(y)
 
 
+@pytest.mark.parametrize("rows,b", [(64, 40), (130, 20), (64, 100)])
+def test_tiled_layout_exact(m, rows, b):
+    """Exact single-term products through the tiled kernel (b > 16, cols a
+    multiple of 512): row r's one non-zero weight, 2^-(r % 8) (code 2 with
+    scale byte 127 - r % 8), sits at column (37 r) % 512, and token t has
+    x[t][c] = 2^-((t + c) % 7) (every 32-element block holds a 1, so MXFP8
+    keeps each value exactly), so y[t][r] = 2^-(r % 8) * 2^-((t + 37 r) % 7)
+    exactly: any slip in the row, token, column or scale lanes changes bits."""
+    cols = 512
+    wmap = {(r, (37 * r) % cols): (2, 127 - r % 8) for r in range(rows)}
+    t = np.arange(b)[:, None]
+    c = np.arange(cols)[None, :]
+    x = np.exp2(-((t + c) % 7)).astype(np.float32)
+    y = crafted(m, wmap, x, rows=rows, cols=cols)
+    r = np.arange(rows)[None, :]
+    want = np.exp2(-(r % 8) - ((t + (37 * r) % cols) % 7)).astype(np.float32)
+    assert np.array_equal(y, want)
+
+
 def test_blocks_add_exactly(m):
     """Products in different 32-element blocks add exactly: 1 + 2^-k."""
     for k in range(1, 24):
