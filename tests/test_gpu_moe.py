@@ -346,3 +346,38 @@ def test_fused_grouping_v41(m, shared):
                                                h_out=h)
     torch.cuda.synchronize()
     assert np.array_equal(host(fused).view(np.uint16), host(staged).view(np.uint16))
+
+
+@pytest.mark.parametrize("T,K,E,xdt", [
+    (8, 6, 64, "f32"),     # at most 64 pairs: grouping inside the gate/up kernel
+    (24, 4, 16, "bf16"),   # grouping kernel, skinny kernels
+    (160, 3, 24, "bf16"),  # tiled kernels
+])
+def test_every_pair_dropped(m, T, K, E, xdt):
+    """The method's degenerate routing: every pair dropped (id -1 or
+    >= n_experts), so there are no work items and every output is an empty
+    weighted sum, +0 in every position (the oracle's combine of no slots).
+    The workspace first serves a call with real routing, so the empty call
+    must replace that call's item list and slot tables, not reuse them; a
+    real call after it gives the first call's bits again.  Plain bank, FP4 x
+    FP8 bank and (bf16) V4.1 bank without a shared expert."""
+    H = I = 512
+    c = inputs.moe_case(4242 + T, E, H, I, T, K, xdt, "softmax", scale_lo=110, scale_hi=124)
+    d = upload(c)
+    dropped = dev(np.where(np.arange(T * K).reshape(T, K) % 2 == 0, -1, E + 3).astype(np.int32))
+    banks = [("plain", m.moe_experts_mxfp4,
+              m.moe_experts_mxfp4_workspace_size(T, K, E, H, I, d["x"].dtype)),
+             ("a8", m.moe_experts_mxfp4_a8, m.moe_experts_mxfp4_a8_workspace_size(T, K, E, H, I))]
+    if xdt == "bf16":
+        banks.append(("v41", lambda *a, **k: m.moe_experts_mxfp4_v41(*a, swiglu_limit=7.0, **k),
+                      m.moe_experts_mxfp4_v41_workspace_size(T, K, E, H, I, False)))
+    for name, fn, need in banks:
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        args = (d["gate"], d["up"], d["down"], E, H, I, d["x"])
+        real = host(fn(*args, d["ids"], d["w"], workspace=ws))
+        empty = host(fn(*args, dropped, d["w"], workspace=ws))
+        again = host(fn(*args, d["ids"], d["w"], workspace=ws))
+        torch.cuda.synchronize()
+        assert real.view(np.uint16).any(), name
+        assert not empty.view(np.uint16).any(), (name, np.count_nonzero(empty.view(np.uint16)))
+        assert np.array_equal(real.view(np.uint16), again.view(np.uint16)), name
