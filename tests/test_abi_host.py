@@ -105,6 +105,9 @@ def status(fn, *args):
     (16, 64, 1, 2, 0, -1),       # bad x dtype
     (16, 64, 1, 0, 7, -1),       # bad y dtype
     (16, 1 << 15, 1, 0, 0, -1),  # cols above the cap
+    ((1 << 24) + 1, 32, 1, 0, 0, -1),  # rows above the cap
+    (246724, 16384, 1, 0, 0, -1),      # tensor bytes above the cap (246723 rows fit)
+    (16, 64, (1 << 20) + 1, 0, 0, -1),  # tokens above the cap
 ])
 def test_gemm_refusals(m, rows, cols, b, xdt, ydt, expect):
     L = m.lib()

@@ -216,3 +216,31 @@ def test_huge_and_infinite_activations(m, orc, rows, cols, b):
     assert np.all(np.isfinite(want[:2]))
     assert_within(y[fin_tok], want, mag, what="huge finite activations")
     assert np.all(np.isnan(y[2])) and np.all(np.isnan(y[3])), "infinite activation"
+
+
+def rows_subtensor(w, rows, cols, sel):
+    """The stored tensor of the rows ``sel`` of a rows x cols tensor (each
+    plane's rows taken in the same order)."""
+    cb = rows * cols // 2
+    codes = w[:cb].reshape(rows, cols // 2)[sel]
+    scales = w[cb:cb + rows * (cols // 32)].reshape(rows, cols // 32)[sel]
+    return np.concatenate([codes.ravel(), scales.ravel()])
+
+
+@pytest.mark.parametrize("rows,cols,b", [(1 << 24, 32, 1), (1 << 24, 32, 8),
+                                         (246723, 16384, 1), (246723, 16384, 8)])
+def test_maximum_sizes(m, orc, rows, cols, b):
+    """The largest accepted tensors: MXFP4_MAX_ROWS rows at the narrowest
+    width, and MXFP4_MAX_COLS columns at the largest row count whose tensor
+    fits MXFP4_MAX_TENSOR_BYTES (246723 x 16384: 2,147,476,992 bytes; one
+    more row is refused).  Every token of the first and last rows, the
+    16-row tile and chunk boundaries and 200 seeded random rows against the
+    oracle on a tensor of just those rows."""
+    assert m.mxfp4_nbytes(rows, cols) <= 1 << 31
+    w, x = inputs.gemm_case(880 + b + cols, rows, cols, b)
+    y = run(m, w, rows, cols, x)
+    rng = np.random.default_rng(rows + b)
+    sel = np.unique(np.concatenate([[0, 1, 15, 16, 17, 63, 64, rows // 2, rows - 17, rows - 16,
+                                     rows - 2, rows - 1], rng.integers(0, rows, 200)]))
+    want, mag = orc.gemm(rows_subtensor(w, rows, cols, sel), len(sel), cols, x)
+    assert_within(y[:, sel], want, mag, what=f"{rows}x{cols} b={b}, {len(sel)} rows")
