@@ -301,7 +301,9 @@ int moe_experts_mxfp4_stages(const void *gate, const void *up, const void *down,
  * swiglu_limit: finite, >= 0; 0 means no limit.  has_shared = 1 applies one
  * more expert, index n_experts, to every token with weight 1 as slot top_k:
  * gate, up and down then hold n_experts + 1 tensors each, the shared one
- * last.  Ids outside [0, n_experts) drop the pair (they never select the
+ * last, and top_k + has_shared <= MXFP4_MAX_TOP_K (the shared expert takes a
+ * slot of its own; the workspace size query returns 0 and the call
+ * MXFP4_EINVAL above that).  Ids outside [0, n_experts) drop the pair (they never select the
  * shared expert).  Summation order and accumulation as in moe_experts_mxfp4;
  * the down outputs of a token's slots are summed in slot order in fp32 and
  * rounded once.  Workspace: at least moe_experts_mxfp4_v41_workspace_size

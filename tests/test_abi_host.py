@@ -219,6 +219,19 @@ def test_router_refusals(m):
     assert call(ids=FAKE + 2) == m.MXFP4_EALIGN
 
 
+def test_v41_slot_cap(m):
+    """V4.1: top_k + has_shared slots per token, at most MXFP4_MAX_TOP_K."""
+    L = m.lib()
+    assert m.moe_experts_mxfp4_v41_workspace_size(4, 31, 40, 512, 256, True) > 0
+    assert m.moe_experts_mxfp4_v41_workspace_size(4, 32, 40, 512, 256, False) > 0
+    assert m.moe_experts_mxfp4_v41_workspace_size(4, 32, 40, 512, 256, True) == 0
+    ws = m.moe_experts_mxfp4_v41_workspace_size(4, 31, 40, 512, 256, True)
+    r = L.moe_experts_mxfp4_v41(FAKE, FAKE, FAKE, 40, 512, 256, FAKE, 4, FAKE, FAKE, 32, 0.0, 1,
+                                FAKE, FAKE, ws * 2, None)
+    assert r == m.MXFP4_EINVAL
+    assert "top_k" in m.mxfp4_last_error()
+
+
 def test_stage_refusals(m):
     L = m.lib()
     ws = m.moe_experts_mxfp4_workspace_size(4, 2, 8, 512, 256, 0)

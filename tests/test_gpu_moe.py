@@ -154,7 +154,8 @@ def hot_expert_sample(ids, n_experts, n_hot=3, tpi=64, n_tokens=32, seed=0):
 @pytest.mark.parametrize("E,H,I,T,K", [(5, 64, 96, 4, 2), (8, 512, 256, 9, 3), (16, 1024, 512, 20, 4),
                                        (3, 96, 160, 1, 3), (33, 2048, 1024, 6, 6),
                                        (4, 512, 1024, 40, 2), (6, 1024, 512, 90, 3),
-                                       (40, 512, 512, 16, 4), (40, 512, 512, 13, 5)])
+                                       (40, 512, 512, 16, 4), (40, 512, 512, 13, 5),
+                                       (64, 512, 256, 2, 32), (40, 512, 256, 6, 32)])
 def test_small_banks(m, orc, xd, E, H, I, T, K):
     # (40, 512, 512, 16, 4) / (40, 512, 512, 13, 5): 64 / 65 pairs, one and
     # two 64-pair tiles of the grouping

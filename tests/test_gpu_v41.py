@@ -150,6 +150,15 @@ def test_dropped_ids_never_reach_the_shared_expert(m, orc):
     check(m, orc, c, E, H, I, 1.0, True)
 
 
+@pytest.mark.parametrize("T,K,shared", [(2, 31, True), (5, 31, True), (3, 32, False)])
+def test_max_top_k(m, orc, T, K, shared):
+    """Slots per token at their cap of 32: 31 routed pairs and the shared
+    expert, or 32 routed pairs (2 tokens: 64 slots, one 64-pair grouping
+    tile; 5 tokens: 160; 3 tokens: 96)."""
+    E, H, I = 40, 512, 256
+    check(m, orc, bank_case(95 + T, E, H, I, T, K, shared), E, H, I, 3.0, shared)
+
+
 @pytest.mark.parametrize("T", [8, 20])
 def test_max_experts_shared_with_dropped_ids(m, orc, T):
     """The largest bank the entry point takes (1023 routed experts and the
