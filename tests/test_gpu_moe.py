@@ -254,13 +254,16 @@ def test_rerun_bitwise(m):
 def test_group_large(m, orc):
     """All three grouping paths: one-wave tile ranking (up to 8 tiles of 64
     pairs), 16-wave tile ranking (up to 128 tiles, histogram within 128 KB
-    of LDS) and chunked counting (beyond); 1024 experts; ids outside [0, E)
-    in a few cases."""
+    of LDS) and chunked counting (beyond, up to the 2^25-pair cap); 1024
+    experts; ids outside [0, E) in a few cases."""
     rng = np.random.default_rng(45)
+    # (the last two: the largest routing the entry points take, 2^20 tokens
+    # x top 32 = 33.5 M pairs on 1024 experts, and 2^20 x 8 with dropped ids)
     for (T, K, E, bad) in [(512, 8, 256, 0), (3000, 4, 1024, 0), (1, 1, 1, 0), (7, 32, 40, 0),
                            (1024, 8, 64, 0), (1024, 8, 512, 0), (20, 4, 1024, 0),
                            (100, 6, 50, 9), (1100, 8, 300, 40), (64, 8, 1024, 5),
-                           (8, 6, 64, 0), (60, 8, 7, 3)]:
+                           (8, 6, 64, 0), (60, 8, 7, 3), (1 << 20, 32, 1024, 0),
+                           (1 << 20, 8, 256, 1000)]:
         ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
         if bad:
             flat = ids.reshape(-1)
@@ -382,3 +385,16 @@ def test_every_pair_dropped(m, T, K, E, xdt):
         assert real.view(np.uint16).any(), name
         assert not empty.view(np.uint16).any(), (name, np.count_nonzero(empty.view(np.uint16)))
         assert np.array_equal(real.view(np.uint16), again.view(np.uint16)), name
+
+
+def test_bank_at_token_cap(m, orc):
+    """The largest token count the entry points take (MXFP4_MAX_TOKENS = 2^20
+    tokens, top 8 of 64 experts: 8.4 M pairs, chunked grouping, skinny
+    kernels) at the narrowest widths (hidden = inter = 32): the grouping
+    exact, h of 300 sampled pairs (the first and last among them), down +
+    combine and end to end for their tokens."""
+    E, H, I, T, K = 64, 32, 32, 1 << 20, 8
+    c = inputs.moe_case(2020, E, H, I, T, K, "f32", "softmax", scale_lo=110, scale_hi=124)
+    rng = np.random.default_rng(7)
+    pairs = np.unique(np.concatenate([[0, 1, T * K - 1], rng.integers(0, T * K, 300)]))
+    check_case(m, orc, c, E, H, I, False, sample_pairs=pairs)
