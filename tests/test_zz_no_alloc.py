@@ -93,3 +93,34 @@ def test_noalloc_refuses_sizes_beyond_the_scratch(m):
     assert "static scratch" in str(e.value)
     torch.cuda.synchronize()
     assert torch.all(out == 3.0)
+
+
+def test_noalloc_at_the_scratch_cap(m):
+    """The largest routing whose scratch fits MXFP4_NOALLOC_SCRATCH_BYTES (16
+    experts of 4096 x 2048, Zipf top 8, fp32; the token count found with the
+    size query) gives the workspace call's bits; one token more is refused
+    before any launch."""
+    E, H, I, K = 16, 4096, 2048, 8
+    cap = m.MXFP4_NOALLOC_SCRATCH_BYTES
+
+    def need(T):
+        return m.moe_experts_mxfp4_workspace_size(T, K, E, H, I, torch.float32)
+
+    lo, hi = 1, 1 << 20
+    while lo < hi:  # the largest T with need(T) <= cap
+        mid = (lo + hi + 1) // 2
+        lo, hi = (mid, hi) if need(mid) <= cap else (lo, mid - 1)
+    T = lo
+    assert need(T) <= cap < need(T + 1)
+    c = inputs.moe_case(62, E, H, I, T, K, "f32", "zipf", scale_lo=100, scale_hi=114)
+    d = upload(c)
+    assert np.array_equal(no_alloc(m, d, E, H, I), with_ws(m, d, E, H, I)), T
+    x1 = torch.zeros((T + 1, H), device="cuda")
+    ids1 = torch.zeros((T + 1, K), dtype=torch.int32, device="cuda")
+    w1 = torch.full((T + 1, K), 0.125, device="cuda")
+    out1 = torch.full((T + 1, H), 3.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(m.Mxfp4Error) as e:
+        m.moe_experts_mxfp4_noalloc(d["gate"], d["up"], d["down"], E, H, I, x1, ids1, w1, out1)
+    assert e.value.status == m.MXFP4_EWORKSPACE
+    torch.cuda.synchronize()
+    assert torch.all(out1 == 3.0)
