@@ -244,3 +244,44 @@ def test_maximum_sizes(m, orc, rows, cols, b):
                                      rows - 2, rows - 1], rng.integers(0, rows, 200)]))
     want, mag = orc.gemm(rows_subtensor(w, rows, cols, sel), len(sel), cols, x)
     assert_within(y[:, sel], want, mag, what=f"{rows}x{cols} b={b}, {len(sel)} rows")
+
+
+def onehot_weights(rows, cols):
+    """Row r holds +1 (E2M1 code 2 under scale 2^0) in column r % cols and
+    zeros elsewhere (codes low nibble first)."""
+    codes = np.zeros((rows, cols), np.uint8)
+    codes[np.arange(rows), np.arange(rows) % cols] = 2
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.full((rows, cols // 32), 127, np.uint8)
+    return np.concatenate([packed.ravel(), scales.ravel()])
+
+
+@pytest.mark.parametrize("rows,cols,b", [(64, 64, 1), (300, 96, 5), (512, 512, 8),
+                                         (4096, 1024, 3), (24576, 512, 32), (14336, 4096, 16)])
+def test_activation_split_bitwise(m, rows, cols, b):
+    """One-hot weights make every output a single fp32 activation carried
+    through the kernels' split: hi = x truncated to bf16, lo = the nearest
+    bf16 to x - hi (exact in fp32), y = hi + lo (exact in fp32), so
+    |y - x| < 2^-15 |x|.  Checked bit for bit on the generic (96 columns),
+    split-K (GEMV and GEMM) and tiled (b = 16, 32) kernels, with activations
+    of every binade from 2^-100 to 2^100 and low mantissa bits all ones."""
+    rng = np.random.default_rng(rows + b)
+    x = (rng.standard_normal((b, cols)) * np.exp2(rng.integers(-100, 100, (b, cols)))).astype(
+        np.float32)
+    # every 7th activation: low 16 mantissa bits all ones (the split's
+    # largest error), random sign, top mantissa bits and normal exponent
+    n = x[:, ::7].size
+    bits = ((rng.integers(0, 2, n, dtype=np.uint32) << np.uint32(31))
+            | (rng.integers(27, 227, n, dtype=np.uint32) << np.uint32(23))
+            | (rng.integers(0, 128, n, dtype=np.uint32) << np.uint32(16)) | np.uint32(0xFFFF))
+    x[:, ::7] = bits.view(np.float32).reshape(x[:, ::7].shape)
+    xb = x.view(np.uint32)
+    hi = (xb & np.uint32(0xFFFF0000)).view(np.float32)
+    rest = (x - hi).astype(np.float32)
+    lo = torch.from_numpy(rest).to(torch.bfloat16).to(torch.float32).numpy()
+    want = (hi + lo).astype(np.float32)
+    assert np.all(np.abs(want - x) < np.ldexp(np.abs(x), -15))
+    y = run(m, onehot_weights(rows, cols), rows, cols, x)
+    exp = want[:, np.arange(rows) % cols]
+    assert np.array_equal(y.view(np.uint32), exp.view(np.uint32)), \
+        int(np.count_nonzero(y.view(np.uint32) != exp.view(np.uint32)))
