@@ -30,6 +30,15 @@
 //    lo in column 8 + i), once per step rather than once per wave and
 //    fragment, behind one more barrier; the MFMA then reads these rows the
 //    way it reads bf16 tokens.
+//  * The expert bank's down product walks two row blocks per workgroup:
+//    the stage ring runs on into the second block (the item's slab again,
+//    the weight rows one block further), and each block's outputs go out
+//    as a fixed number of stores per wave (rows and tokens past the end
+//    clamped to the last ones, whose values those lanes hold too), so the
+//    waits stay constants: the first two steps after a block's stores count
+//    them as well.  The blocks are written out one after the other rather
+//    than looped over, so that every path reaching a wait issued the same
+//    loads and stores before it and the compiler adds no waits of its own.
 //  * Work items come from the same grouping as the skinny kernel
 //    ("rlx-cpu 0.2.17, src/gguf_matmul.rs", grouped_moe_sort_plan): an
 //    expert's rows are streamed once per item of up to 16 * NC tokens
@@ -45,6 +54,13 @@ namespace mx {
 namespace {
 
 constexpr int TKS = 128; // columns per K step
+// Row blocks per workgroup in the expert bank's down product: the ring of
+// LDS stages runs on from one block into the next (same item, same token
+// rows, the weight rows RB further on), so a workgroup's start-up loads are
+// paid once per two blocks (measured, 256-expert prefill layer: 1389 ->
+// 1369 us median; three and four blocks per workgroup lost to the longer
+// last round: +12 / +17 us against two)
+constexpr int WALK_DOWN = 2;
 constexpr int TNS = 4;   // LDS stages (= steps per 512-column unit)
 
 template <int N> struct IntTag {
@@ -127,20 +143,26 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     // items (the grid is sized by an upper bound; the surplus workgroups,
     // dispatched last, exit), so the resident workgroups stream adjacent
     // blocks of a few experts' matrices (measured, 256-expert prefill layer:
-    // 1563 us with XCD-grouped ids, 1528 us in dispatch order).
-    int sub, row0;
+    // 1563 us with XCD-grouped ids, 1528 us in dispatch order).  The down
+    // product's workgroups each take WALK consecutive row blocks of their
+    // item (nblk: fewer at the matrix's end).
+    constexpr int WALK = MODE == MODE_DOWN ? WALK_DOWN : 1;
+    static_assert(WALK >= 1 && WALK <= 4, "row blocks per workgroup");
+    int sub, row0, nblk = 1;
     if (MODE == MODE_GEMM) {
         const int lid = xcd_logical(blockIdx.x, gridDim.x);
         sub = lid % a.nch;
         row0 = (lid / a.nch) * RB;
     } else {
         const int nrb = (R + RB - 1) / RB;
-        const int real = *a.n_work * nrb;
+        const int nrbw = (nrb + WALK - 1) / WALK;
+        const int real = *a.n_work * nrbw;
         if ((int)blockIdx.x >= real)
             return;
         const int lid = blockIdx.x;
-        sub = lid / nrb;
-        row0 = (lid % nrb) * RB;
+        sub = lid / nrbw;
+        row0 = (lid % nrbw) * WALK * RB;
+        nblk = min(WALK, nrb - (lid % nrbw) * WALK);
     }
     int ntok, slot0, expert = 0;
     if (MODE == MODE_GEMM) {
@@ -191,6 +213,16 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     // tile ls % MT (lanes of a repeated tile load the same bytes)
     const int smt = ls % MT;
     const uint8_t *ssrc = Am[smt / RT] + code_bytes + (int64_t)lrow(smt % RT) * gpr;
+    // a walking workgroup's later blocks: the same lanes, RB rows further
+    auto code_src_blk = [&] __device__(int bk, int mt, int i) -> const uint8_t * {
+        const int lr = 8 * i + (lane >> 3);
+        const int r = min(row0 + bk * RB + (wave * RT + mt % RT) * 16 + lr, R - 1);
+        return Am[mt / RT] + (int64_t)r * (C / 2) + ((lane & 7) ^ ((lr >> 1) & 7)) * 16;
+    };
+    auto scale_src_blk = [&] __device__(int bk) -> const uint8_t * {
+        const int r = min(row0 + bk * RB + (wave * RT + smt % RT) * 16 + li, R - 1);
+        return Am[smt / RT] + code_bytes + (int64_t)r * gpr;
+    };
     // acc: the current 512-column unit, its 16 MFMA steps in k order; tot:
     // the units so far, summed in ascending order
     f32x4 acc[MT][NC], tot[MT][NC];
@@ -231,18 +263,26 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
         }
         // the codes of pair q (steps 2q, 2q + 1; clamped to the last pair,
         // whose data is then not read) into the buffer of its parity
+        const int npb = nsteps / 2; // pairs per block
         auto issue_codes = [&] __device__(auto pbt, int q) {
             uint8_t *P = pairbuf(pbt);
-            const int qc = min(q, nsteps / 2 - 1);
+            const int qc = min(q, nblk * npb - 1);
+            const int bk = WALK == 1 ? 0 : qc / npb, qb = qc - bk * npb;
+            // (a later block: the same lanes' rows RB further on, so one
+            // address step per block unless the rows clamp at the end)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    lds_dma16(csrc[mt][i] + qc * TKS, P + (wave * MT + mt) * 2048 + i * 1024);
+                    lds_dma16((WALK == 1 ? csrc[mt][i] : code_src_blk(bk, mt, i)) + qb * TKS,
+                              P + (wave * MT + mt) * 2048 + i * 1024);
         };
         // step s's slab (and its codes without pairs; with a unit's first
         // step the unit's scales)
-        auto issue = [&] __device__(auto tag, int s) {
+        auto issue = [&] __device__(auto tag, int g) {
+            // g: the walk's step (block g / nsteps, step g % nsteps of it)
+            const int bk = WALK == 1 ? 0 : g / nsteps;
+            const int s = g - bk * nsteps;
             uint8_t *S = stage(tag);
             if constexpr (!PAIRS) {
 #pragma unroll
@@ -253,8 +293,9 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
             for (int i = 0; i < AIN; ++i)
                 lds_dma16(xsrc[i] + s * ROWB, S + ACT_OFF + (wave * AIN + i) * 1024);
             if constexpr (decltype(tag)::value == 0) // a unit's first step: its scales
-                lds_dma16(ssrc + (s / 4) * 16, scs + wave * 1024);
+                lds_dma16((WALK == 1 ? ssrc : scale_src_blk(bk)) + (s / 4) * 16, scs + wave * 1024);
         };
+        const int gsteps = nblk * nsteps; // the walk's steps
 
         // prologue: the token gathers above have landed; pair 0's codes and
         // steps 0..2 in flight
@@ -262,14 +303,17 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
         if constexpr (PAIRS)
             issue_codes(IntTag<0>{}, 0);
         issue(IntTag<0>{}, 0);
-        issue(IntTag<1>{}, min(1, nsteps - 1));
-        issue(IntTag<2>{}, min(2, nsteps - 1));
+        issue(IntTag<1>{}, min(1, gsteps - 1));
+        issue(IntTag<2>{}, min(2, gsteps - 1));
 
         u32x4 usc[MT]; // scale bytes of the current unit: word j = step j
-        for (int un = 0; un < nunits; ++un) {
+        // unit un of the walk; AFTER_STORE: a later block's first unit, whose
+        // steps 0 and 1 wait behind the previous block's output stores too
+        auto unit = [&] __device__(int un, auto ast) {
+            constexpr bool after_store = decltype(ast)::value != 0;
             auto step = [&] __device__(auto jt) {
                 constexpr int j = decltype(jt)::value;
-                const int s = un * TNS + j;
+                const int s = un * TNS + j; // the walk's step
                 // stage j (step s) and the codes of this step's pair have
                 // landed for every wave; stage j - 1 (step s - 1) is free, and
                 // at an even step so is the other pair buffer.  Issued at
@@ -288,12 +332,16 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
                 // (this wave's LDS reads of the previous step, which was
                 // stage j - 1, the one refilled below, are done before the
                 // barrier: the barrier itself orders no memory)
-                wait_vmcnt<AHEAD>();
+                constexpr int S_ST = WALK > 1 ? RT * NCU * 4 : 0; // stores per block
+                if constexpr (j < 2 && after_store)
+                    wait_vmcnt<AHEAD + S_ST>();
+                else
+                    wait_vmcnt<AHEAD>();
                 wait_lgkm0();
                 raw_barrier();
                 if constexpr (PAIRS && j % 2 == 0)
                     issue_codes(IntTag<(j / 2 + 1) % 2>{}, s / 2 + 1);
-                issue(IntTag<(j + 3) % TNS>{}, min(s + 3, nsteps - 1));
+                issue(IntTag<(j + 3) % TNS>{}, min(s + 3, gsteps - 1));
 
                 const uint8_t *S = stage(IntTag<j>{});
                 if constexpr (!XBF) {
@@ -369,13 +417,62 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
             step(IntTag<2>{});
             step(IntTag<3>{});
             // ---- end of a 512-column unit
+            const int ub = WALK == 1 ? un : un % nunits;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int c = 0; c < NCU; ++c) {
-                    tot[mt][c] = un == 0 ? acc[mt][c] : tot[mt][c] + acc[mt][c];
+                    tot[mt][c] = ub == 0 ? acc[mt][c] : tot[mt][c] + acc[mt][c];
                     acc[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
+        };
+        // a block's outputs: a fixed number of stores per wave (RT * NCU * 4),
+        // rows past the end and tokens past the item clamped to the last ones,
+        // whose values those lanes hold too (their A rows and B columns were
+        // loaded clamped the same way)
+        auto block_out = [&] __device__(int bk) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int c = 0; c < NCU; ++c) {
+                    f32x4 g = tot[rt][c];
+                    if (!XBF) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            g[i] += dpp_row_ror8(g[i]);
+                    }
+                    const int tok = min(XBF ? c * 16 + li : c * 8 + (li & 7), ntok - 1);
+                    const int64_t orow = slot0 + tok;
+                    const int rbase = row0 + bk * RB + (wave * RT + rt) * 16 + 4 * ls;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        reinterpret_cast<float *>(a.y)[orow * R + min(rbase + i, R - 1)] = g[i];
+                }
+        };
+        // the blocks written out one after the other (no loop around them,
+        // so that every path to a wait has the same loads and stores before
+        // it and the constant waits above are the only ones)
+        if constexpr (WALK == 1) {
+            for (int un = 0; un < nunits; ++un)
+                unit(un, IntTag<0>{});
+        } else {
+            for (int un = 0; un < nunits; ++un)
+                unit(un, IntTag<0>{});
+            block_out(0);
+            auto later = [&] __device__(auto bt) {
+                constexpr int bk = decltype(bt)::value;
+                if constexpr (bk < WALK) {
+                    if (nblk > bk) {
+                        unit(bk * nunits, IntTag<1>{});
+                        for (int un = bk * nunits + 1; un < (bk + 1) * nunits; ++un)
+                            unit(un, IntTag<0>{});
+                        block_out(bk);
+                    }
+                }
+            };
+            later(IntTag<1>{});
+            later(IntTag<2>{});
+            later(IntTag<3>{});
         }
     };
     if (NC >= 4 && nct >= 4)
@@ -390,6 +487,8 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(SkinnyArgs a)
     wait_vmcnt<0>();
 
     // ---- outputs
+    if constexpr (WALK > 1)
+        return;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
@@ -487,7 +586,8 @@ hipError_t tiled_launch(int mode, bool xbf, int nw, int rt, int nc, const Skinny
         return hipErrorInvalidValue;
     const int rpw = tiled_rows_per_wg(nw, rt);
     const int64_t nrb = (a.rows + rpw - 1) / rpw;
-    hipLaunchKernelGGL(e->fn, dim3((unsigned)(nrb * a.nch)), dim3(nw * 64), 0, stream, a);
+    const int64_t nrbw = mode == MODE_DOWN ? (nrb + WALK_DOWN - 1) / WALK_DOWN : nrb;
+    hipLaunchKernelGGL(e->fn, dim3((unsigned)(nrbw * a.nch)), dim3(nw * 64), 0, stream, a);
     return hipGetLastError();
 }
 
